@@ -1,0 +1,238 @@
+"""ctypes binding of libpba.so: argument marshalling only.
+
+Torch tensors supply device memory and the current HIP stream; every step
+of the computation runs in the library's kernels.  Importing this module
+fails loudly if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpba.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m block_sparse_attention_pack_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+PBA_OK = 0
+TILE_SKIP, TILE_PARTIAL, TILE_FULL = 0, 1, 2
+EXPORTED = ("pba_strerror", "pba_fwd_tile", "pba_bwd_tile", "pba_map_bytes", "pba_map_init",
+            "pba_pack_block_map", "pba_packed_attn_fwd", "pba_bwd_workspace_bytes", "pba_packed_attn_bwd")
+
+
+class PbaBlockMap(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("S", ctypes.c_int32), ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
+        ("nqt", ctypes.c_int32), ("nkt", ctypes.c_int32),
+        ("tok_pack", ctypes.c_void_p), ("tok_branch", ctypes.c_void_p), ("tok_win", ctypes.c_void_p),
+        ("cls", ctypes.c_void_p), ("q2k_cnt", ctypes.c_void_p), ("q2k_idx", ctypes.c_void_p),
+        ("k2q_cnt", ctypes.c_void_p), ("k2q_idx", ctypes.c_void_p), ("totals", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
+    ]
+
+
+_c_int_p = ctypes.POINTER(ctypes.c_int)
+_lib.pba_strerror.argtypes = [ctypes.c_int]
+_lib.pba_strerror.restype = ctypes.c_char_p
+for _n in ("pba_fwd_tile", "pba_bwd_tile"):
+    getattr(_lib, _n).argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _c_int_p, _c_int_p]
+    getattr(_lib, _n).restype = ctypes.c_int
+_lib.pba_map_bytes.argtypes = [ctypes.c_int] * 4
+_lib.pba_map_bytes.restype = ctypes.c_size_t
+_lib.pba_map_init.argtypes = [ctypes.POINTER(PbaBlockMap), ctypes.c_void_p, ctypes.c_size_t] + [ctypes.c_int] * 4
+_lib.pba_map_init.restype = ctypes.c_int
+_lib.pba_pack_block_map.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.POINTER(PbaBlockMap), ctypes.c_void_p]
+_lib.pba_pack_block_map.restype = ctypes.c_int
+_lib.pba_packed_attn_fwd.argtypes = [ctypes.POINTER(PbaBlockMap)] + [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + \
+    [ctypes.c_float, ctypes.c_void_p]
+_lib.pba_packed_attn_fwd.restype = ctypes.c_int
+_lib.pba_bwd_workspace_bytes.argtypes = [ctypes.c_int] * 4
+_lib.pba_bwd_workspace_bytes.restype = ctypes.c_size_t
+_lib.pba_packed_attn_bwd.argtypes = [ctypes.POINTER(PbaBlockMap)] + [ctypes.c_void_p] * 10 + [ctypes.c_size_t] + \
+    [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_void_p]
+_lib.pba_packed_attn_bwd.restype = ctypes.c_int
+
+
+class PbaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} (code {code})")
+
+
+def strerror(code: int) -> str:
+    return _lib.pba_strerror(int(code)).decode()
+
+
+def _check(rc: int, where: str):
+    if rc != PBA_OK:
+        raise PbaError(rc, where)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def fwd_tile(Hq: int, Hkv: int, D: int) -> Tuple[int, int]:
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    _check(_lib.pba_fwd_tile(Hq, Hkv, D, ctypes.byref(bm), ctypes.byref(bn)), "pba_fwd_tile")
+    return bm.value, bn.value
+
+
+def bwd_tile(Hq: int, Hkv: int, D: int) -> Tuple[int, int]:
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    _check(_lib.pba_bwd_tile(Hq, Hkv, D, ctypes.byref(bm), ctypes.byref(bn)), "pba_bwd_tile")
+    return bm.value, bn.value
+
+
+def map_bytes(B: int, S: int, block_m: int, block_n: int) -> int:
+    return int(_lib.pba_map_bytes(B, S, block_m, block_n))
+
+
+def workspace_bytes(B: int, S: int, Hq: int, D: int) -> int:
+    return int(_lib.pba_bwd_workspace_bytes(B, S, Hq, D))
+
+
+class BlockMap:
+    """A device block map: one torch uint8 buffer carved by pba_map_init."""
+
+    def __init__(self, B: int, S: int, block_m: int, block_n: int, device="cuda"):
+        nbytes = map_bytes(B, S, block_m, block_n)
+        if nbytes == 0:
+            raise PbaError(-2, "pba_map_bytes")
+        self.buffer = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        base = self.buffer.data_ptr()
+        self._off0 = (-base) % 256
+        self.struct = PbaBlockMap()
+        _check(_lib.pba_map_init(ctypes.byref(self.struct), base + self._off0, nbytes, B, S, block_m, block_n),
+               "pba_map_init")
+        self.B, self.S, self.block_m, self.block_n = B, S, block_m, block_n
+        self.nqt, self.nkt = self.struct.nqt, self.struct.nkt
+
+    def _view(self, field: str, n: int, dtype) -> torch.Tensor:
+        off = getattr(self.struct, field) - self.buffer.data_ptr()
+        esz = torch.empty((), dtype=dtype).element_size()
+        return self.buffer[off:off + n * esz].view(dtype)
+
+    # Views of the map fields (device tensors), shaped like their definitions.
+    def tok_pack(self):
+        return self._view("tok_pack", self.B * self.S, torch.int32).view(self.B, self.S)
+
+    def tok_branch(self):
+        return self._view("tok_branch", self.B * self.S, torch.int32).view(self.B, self.S)
+
+    def tok_win(self):
+        return self._view("tok_win", self.B * self.S * 4, torch.int32).view(self.B, self.S, 4)
+
+    def cls(self):
+        return self._view("cls", self.B * self.nqt * self.nkt, torch.uint8).view(self.B, self.nqt, self.nkt)
+
+    def q2k_cnt(self):
+        return self._view("q2k_cnt", self.B * self.nqt * 2, torch.int32).view(self.B, self.nqt, 2)
+
+    def q2k_idx(self):
+        return self._view("q2k_idx", self.B * self.nqt * self.nkt, torch.int32).view(self.B, self.nqt, self.nkt)
+
+    def k2q_cnt(self):
+        return self._view("k2q_cnt", self.B * self.nkt * 2, torch.int32).view(self.B, self.nkt, 2)
+
+    def k2q_idx(self):
+        return self._view("k2q_idx", self.B * self.nkt * self.nqt, torch.int32).view(self.B, self.nkt, self.nqt)
+
+    def totals(self):
+        return self._view("totals", 3, torch.int64)
+
+    def status(self):
+        return self._view("status", 2, torch.int32)
+
+    def to_host(self) -> dict:
+        """Every field as numpy (synchronises)."""
+        return {
+            "B": self.B, "S": self.S, "block_m": self.block_m, "block_n": self.block_n,
+            "nqt": self.nqt, "nkt": self.nkt,
+            "tok_pack": self.tok_pack().cpu().numpy(), "tok_branch": self.tok_branch().cpu().numpy(),
+            "tok_win": self.tok_win().cpu().numpy(), "cls": self.cls().cpu().numpy(),
+            "q2k_cnt": self.q2k_cnt().cpu().numpy(), "q2k_idx": self.q2k_idx().cpu().numpy(),
+            "k2q_cnt": self.k2q_cnt().cpu().numpy(), "k2q_idx": self.k2q_idx().cpu().numpy(),
+            "totals": self.totals().cpu().numpy(), "status": self.status().cpu().numpy(),
+        }
+
+
+def descriptors_to_device(packs, resp_len, device="cuda") -> Tuple[torch.Tensor, torch.Tensor]:
+    """int32 [P, 5] descriptor table and [R] response lengths as device tensors."""
+    p = torch.as_tensor(packs, dtype=torch.int32).reshape(-1, 5).contiguous().to(device)
+    r = torch.as_tensor(resp_len, dtype=torch.int32).reshape(-1).contiguous().to(device)
+    return p, r
+
+
+def pack_block_map(packs_dev: torch.Tensor, resp_len_dev: torch.Tensor, B: int, S: int, block_m: int, block_n: int,
+                   out: Optional[BlockMap] = None, stream=None) -> BlockMap:
+    """pba_pack_block_map on device descriptors (int32 [P, 5] and [R])."""
+    m = out if out is not None else BlockMap(B, S, block_m, block_n, device=packs_dev.device)
+    assert packs_dev.dtype == torch.int32 and resp_len_dev.dtype == torch.int32
+    n_packs = packs_dev.shape[0] if packs_dev.numel() else 0
+    n_resp = resp_len_dev.numel()
+    _check(_lib.pba_pack_block_map(packs_dev.data_ptr() if n_packs else None, n_packs,
+                                   resp_len_dev.data_ptr() if n_resp else None, n_resp,
+                                   ctypes.byref(m.struct), _stream(stream)), "pba_pack_block_map")
+    return m
+
+
+def _bf16(x: torch.Tensor, name: str):
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bf16 device tensor")
+
+
+def packed_attn_fwd(m: BlockMap, q, k, v, softmax_scale: Optional[float] = None,
+                    out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None, stream=None):
+    """O [B, S, Hq, D] bf16 and LSE [B, Hq, S] fp32."""
+    for n, x in (("q", q), ("k", k), ("v", v)):
+        _bf16(x, n)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, S, Hkv, D) or v.shape != k.shape:
+        raise ValueError("k / v shape mismatch")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    _check(_lib.pba_packed_attn_fwd(ctypes.byref(m.struct), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    lse.data_ptr(), B, S, Hq, Hkv, D, scale, _stream(stream)), "pba_packed_attn_fwd")
+    return o, lse
+
+
+def packed_attn_bwd(m: BlockMap, q, k, v, o, lse, dout, softmax_scale: Optional[float] = None,
+                    out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None):
+    """dQ, dK, dV (bf16) for the loss <dO, O>."""
+    for n, x in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _bf16(x, n)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+    need = workspace_bytes(B, S, Hq, D)
+    if workspace is None:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+    base = workspace.data_ptr()
+    off = (-base) % 256
+    _check(_lib.pba_packed_attn_bwd(ctypes.byref(m.struct), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                    base + off, workspace.numel() - off, B, S, Hq, Hkv, D, scale, _stream(stream)),
+           "pba_packed_attn_bwd")
+    return dq, dk, dv

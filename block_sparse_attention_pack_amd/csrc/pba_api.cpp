@@ -1,0 +1,266 @@
+// C ABI entry points: argument checks, map buffer carving, kernel launches.
+// Nothing here allocates or synchronises; all work goes to the caller's
+// stream.  Descriptor contents are checked on the device by the map kernels.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+
+#include "pba_internal.h"
+
+namespace pba {
+int fwd_wg_heads(int G);
+}
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxB = 65535;
+constexpr int kMaxS = 1 << 22;
+constexpr int kMaxHeads = 4096;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool tile_ok(int t) { return t == 16 || t == 32 || t == 64 || t == 128 || t == 256; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Field sizes of a map, in the order they are carved from the buffer.
+struct MapLayout {
+  size_t off[10];
+  size_t total;
+};
+
+MapLayout map_layout(int B, int S, int bm, int bn) {
+  const size_t nqt = (size_t)((S + bm - 1) / bm), nkt = (size_t)((S + bn - 1) / bn);
+  const size_t ntok = (size_t)B * S;
+  const size_t sizes[10] = {
+      4 * ntok,               // tok_pack
+      4 * ntok,               // tok_branch
+      16 * ntok,              // tok_win
+      (size_t)B * nqt * nkt,  // cls
+      8 * (size_t)B * nqt,    // q2k_cnt
+      4 * (size_t)B * nqt * nkt,  // q2k_idx
+      8 * (size_t)B * nkt,    // k2q_cnt
+      4 * (size_t)B * nkt * nqt,  // k2q_idx
+      3 * 8,                  // totals
+      2 * 4,                  // status
+  };
+  MapLayout L;
+  size_t o = 0;
+  for (int i = 0; i < 10; ++i) {
+    L.off[i] = o;
+    o += align_up(sizes[i]);
+  }
+  L.total = o;
+  return L;
+}
+
+// gfx950 check, cached per device.
+int device_ok() {
+  static std::mutex mu;
+  static int cache[64];
+  static bool init = false;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return PBA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!init) {
+    for (int i = 0; i < 64; ++i) cache[i] = 0;
+    init = true;
+  }
+  if (cache[dev] == 0) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return PBA_ERR_DEVICE;
+    cache[dev] = (std::strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+  }
+  return cache[dev] == 1 ? PBA_OK : PBA_ERR_DEVICE;
+}
+
+int check_map(const pba_block_map* m, int B, int S, int bm, int bn) {
+  if (!m || !m->tok_win || !m->q2k_cnt || !m->q2k_idx || !m->k2q_cnt || !m->k2q_idx || !m->status) return PBA_ERR_NULL;
+  if (m->B != B || m->S != S) return PBA_ERR_MAP;
+  if (m->block_m != bm || m->block_n != bn) return PBA_ERR_TILE;
+  if (m->nqt != (S + bm - 1) / bm || m->nkt != (S + bn - 1) / bn) return PBA_ERR_MAP;
+  return PBA_OK;
+}
+
+int check_heads(int B, int S, int Hq, int Hkv, int D) {
+  if (B < 1 || B > kMaxB || S < 1 || S > kMaxS || Hq < 1 || Hkv < 1 || Hq > kMaxHeads) return PBA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return PBA_ERR_HEADS;
+  if (D != 64 && D != 128) return PBA_ERR_HEAD_DIM;
+  return PBA_OK;
+}
+
+pba::MapView view_of(const pba_block_map* m) {
+  pba::MapView v;
+  v.B = m->B; v.S = m->S; v.bm = m->block_m; v.bn = m->block_n; v.nqt = m->nqt; v.nkt = m->nkt;
+  v.tok_win = m->tok_win; v.q2k_cnt = m->q2k_cnt; v.q2k_idx = m->q2k_idx;
+  v.k2q_cnt = m->k2q_cnt; v.k2q_idx = m->k2q_idx; v.status = m->status;
+  return v;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pba_strerror(int code) {
+  switch (code) {
+    case PBA_OK: return "ok";
+    case PBA_ERR_NULL: return "a required pointer is NULL";
+    case PBA_ERR_SHAPE: return "B, S, pack count or head count out of range";
+    case PBA_ERR_HEADS: return "Hq is not a multiple of Hkv";
+    case PBA_ERR_HEAD_DIM: return "head dim must be 64 or 128";
+    case PBA_ERR_TILE: return "tile shape unsupported or map built for another tile shape";
+    case PBA_ERR_MAP: return "map built for another (B, S) or its buffer is too small";
+    case PBA_ERR_WORKSPACE: return "backward workspace missing or too small";
+    case PBA_ERR_DEVICE: return "no gfx950 device current, or a HIP launch failed";
+    case PBA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case PBA_DESC_ROW: return "descriptor: row outside [0, B)";
+    case PBA_DESC_NEGATIVE: return "descriptor: negative start, length or response count";
+    case PBA_DESC_RESP_RANGE: return "descriptor: response range outside resp_len";
+    case PBA_DESC_BOUNDS: return "descriptor: pack runs past the end of its row";
+    case PBA_DESC_ORDER: return "descriptor: packs not sorted by (row, start) or overlapping";
+    default: return "unknown code";
+  }
+}
+
+int pba_fwd_tile(int Hq, int Hkv, int D, int* block_m, int* block_n) {
+  if (!block_m || !block_n) return PBA_ERR_NULL;
+  if (Hq < 1 || Hkv < 1 || Hq > kMaxHeads) return PBA_ERR_SHAPE;
+  if (Hq % Hkv) return PBA_ERR_HEADS;
+  if (D != 64 && D != 128) return PBA_ERR_HEAD_DIM;
+  *block_m = pba::kFwdBM * (4 / pba::fwd_wg_heads(Hq / Hkv));
+  *block_n = pba::kFwdBN;
+  return PBA_OK;
+}
+
+int pba_bwd_tile(int Hq, int Hkv, int D, int* block_m, int* block_n) {
+  if (!block_m || !block_n) return PBA_ERR_NULL;
+  if (Hq < 1 || Hkv < 1 || Hq > kMaxHeads) return PBA_ERR_SHAPE;
+  if (Hq % Hkv) return PBA_ERR_HEADS;
+  if (D != 64 && D != 128) return PBA_ERR_HEAD_DIM;
+  *block_m = pba::kBwdBM;
+  *block_n = pba::kBwdBN;
+  return PBA_OK;
+}
+
+size_t pba_map_bytes(int B, int S, int block_m, int block_n) {
+  if (B < 1 || B > kMaxB || S < 1 || S > kMaxS || !tile_ok(block_m) || !tile_ok(block_n)) return 0;
+  return map_layout(B, S, block_m, block_n).total;
+}
+
+int pba_map_init(pba_block_map* map, void* buffer, size_t buffer_bytes, int B, int S, int block_m, int block_n) {
+  if (!map || !buffer) return PBA_ERR_NULL;
+  if (B < 1 || B > kMaxB || S < 1 || S > kMaxS) return PBA_ERR_SHAPE;
+  if (!tile_ok(block_m) || !tile_ok(block_n)) return PBA_ERR_TILE;
+  if ((reinterpret_cast<uintptr_t>(buffer) & (kAlign - 1)) != 0) return PBA_ERR_ALIGN;
+  const MapLayout L = map_layout(B, S, block_m, block_n);
+  if (buffer_bytes < L.total) return PBA_ERR_MAP;
+  char* base = static_cast<char*>(buffer);
+  map->B = B;
+  map->S = S;
+  map->block_m = block_m;
+  map->block_n = block_n;
+  map->nqt = (S + block_m - 1) / block_m;
+  map->nkt = (S + block_n - 1) / block_n;
+  map->tok_pack = reinterpret_cast<int32_t*>(base + L.off[0]);
+  map->tok_branch = reinterpret_cast<int32_t*>(base + L.off[1]);
+  map->tok_win = reinterpret_cast<int32_t*>(base + L.off[2]);
+  map->cls = reinterpret_cast<uint8_t*>(base + L.off[3]);
+  map->q2k_cnt = reinterpret_cast<int32_t*>(base + L.off[4]);
+  map->q2k_idx = reinterpret_cast<int32_t*>(base + L.off[5]);
+  map->k2q_cnt = reinterpret_cast<int32_t*>(base + L.off[6]);
+  map->k2q_idx = reinterpret_cast<int32_t*>(base + L.off[7]);
+  map->totals = reinterpret_cast<int64_t*>(base + L.off[8]);
+  map->status = reinterpret_cast<int32_t*>(base + L.off[9]);
+  return PBA_OK;
+}
+
+int pba_pack_block_map(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,
+                       const pba_block_map* map, void* stream) {
+  if (!map || !map->tok_pack || !map->tok_branch || !map->tok_win || !map->cls || !map->q2k_cnt || !map->q2k_idx ||
+      !map->k2q_cnt || !map->k2q_idx || !map->totals || !map->status)
+    return PBA_ERR_NULL;
+  if (n_packs < 0 || n_resp_total < 0) return PBA_ERR_SHAPE;
+  if ((n_packs > 0 && !packs) || (n_resp_total > 0 && !resp_len)) return PBA_ERR_NULL;
+  if (map->B < 1 || map->B > kMaxB || map->S < 1 || map->S > kMaxS) return PBA_ERR_SHAPE;
+  if (!tile_ok(map->block_m) || !tile_ok(map->block_n)) return PBA_ERR_TILE;
+  if (map->nqt != (map->S + map->block_m - 1) / map->block_m || map->nkt != (map->S + map->block_n - 1) / map->block_n)
+    return PBA_ERR_MAP;
+  if (int rc = device_ok()) return rc;
+  hipError_t e = pba::launch_map(packs, n_packs, resp_len, n_resp_total, *map, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PBA_OK : PBA_ERR_DEVICE;
+}
+
+int pba_packed_attn_fwd(const pba_block_map* map, const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int S, int Hq, int Hkv, int D, float softmax_scale, void* stream) {
+  if (!q || !k || !v || !o || !lse) return PBA_ERR_NULL;
+  if (int rc = check_heads(B, S, Hq, Hkv, D)) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return PBA_ERR_ALIGN;
+  int bm, bn;
+  pba_fwd_tile(Hq, Hkv, D, &bm, &bn);
+  if (int rc = check_map(map, B, S, bm, bn)) return rc;
+  if (int rc = device_ok()) return rc;
+  pba::FwdArgs a;
+  a.map = view_of(map);
+  a.q = static_cast<const pba::bf16*>(q);
+  a.k = static_cast<const pba::bf16*>(k);
+  a.v = static_cast<const pba::bf16*>(v);
+  a.o = static_cast<pba::bf16*>(o);
+  a.lse = lse;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.wg_heads = pba::fwd_wg_heads(a.G);
+  a.scale_log2 = softmax_scale * pba::kLog2eHost;
+  hipError_t e = pba::launch_fwd(a, D, B, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PBA_OK : PBA_ERR_DEVICE;
+}
+
+size_t pba_bwd_workspace_bytes(int B, int S, int Hq, int D) {
+  if (B < 1 || B > kMaxB || S < 1 || S > kMaxS || Hq < 1 || Hq > kMaxHeads || (D != 64 && D != 128)) return 0;
+  return align_up((size_t)B * S * Hq * D * 4) + align_up((size_t)B * Hq * S * 4);
+}
+
+int pba_packed_attn_bwd(const pba_block_map* map, const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                        size_t workspace_bytes, int B, int S, int Hq, int Hkv, int D, float softmax_scale,
+                        void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return PBA_ERR_NULL;
+  if (int rc = check_heads(B, S, Hq, Hkv, D)) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return PBA_ERR_ALIGN;
+  int bm, bn;
+  pba_bwd_tile(Hq, Hkv, D, &bm, &bn);
+  if (int rc = check_map(map, B, S, bm, bn)) return rc;
+  const size_t need = pba_bwd_workspace_bytes(B, S, Hq, D);
+  if (!workspace || workspace_bytes < need) return PBA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return PBA_ERR_ALIGN;
+  if (int rc = device_ok()) return rc;
+  pba::BwdArgs a;
+  a.map = view_of(map);
+  a.q = static_cast<const pba::bf16*>(q);
+  a.k = static_cast<const pba::bf16*>(k);
+  a.v = static_cast<const pba::bf16*>(v);
+  a.o = static_cast<const pba::bf16*>(o);
+  a.lse = lse;
+  a.dout = static_cast<const pba::bf16*>(dout);
+  a.dq = static_cast<pba::bf16*>(dq);
+  a.dk = static_cast<pba::bf16*>(dk);
+  a.dv = static_cast<pba::bf16*>(dv);
+  a.dq_acc = static_cast<float*>(workspace);
+  a.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up((size_t)B * S * Hq * D * 4));
+  a.B = B;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * pba::kLog2eHost;
+  hipError_t e = pba::launch_bwd(a, D, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PBA_OK : PBA_ERR_DEVICE;
+}
+
+}  // extern "C"

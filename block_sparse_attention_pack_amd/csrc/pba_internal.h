@@ -1,0 +1,72 @@
+// Internal declarations shared by the library's translation units (not part
+// of the C ABI).  gfx950 only: wave64, bf16 MFMA, LDS transpose reads.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pba.h"
+
+namespace pba {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define PBA_LDS __attribute__((address_space(3)))
+
+// Tile shapes of the attention kernels (query tokens x key tokens).
+constexpr int kFwdBM = 64;   // one wave owns 64 query rows of one q head
+constexpr int kFwdBN = 64;
+constexpr int kBwdBM = 64;   // query rows per backward step
+constexpr int kBwdBN = 128;  // key rows per backward workgroup (4 waves x 32)
+
+struct MapView {  // device-side view of a pba_block_map
+  int B, S, bm, bn, nqt, nkt;
+  const int32_t* tok_win;
+  const int32_t* q2k_cnt;
+  const int32_t* q2k_idx;
+  const int32_t* k2q_cnt;
+  const int32_t* k2q_idx;
+  const int32_t* status;
+};
+
+struct FwdArgs {
+  MapView map;
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  bf16* o;
+  float* lse;
+  int S, Hq, Hkv, G, wg_heads;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+struct BwdArgs {
+  MapView map;
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const bf16* o;
+  const float* lse;
+  const bf16* dout;
+  bf16* dq;
+  bf16* dk;
+  bf16* dv;
+  float* dq_acc;  // [B, S, Hq, D] fp32
+  float* delta;   // [B, Hq, S]  fp32 rowsum(dO * O)
+  int B, S, Hq, Hkv, G;
+  float scale, scale_log2;
+};
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_map(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,
+                      const pba_block_map& map, hipStream_t stream);
+hipError_t launch_fwd(const FwdArgs& a, int D, int B, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int D, hipStream_t stream);
+
+}  // namespace pba

@@ -1,0 +1,188 @@
+/*
+ * pba.h -- packed branch-aware attention on MI355X (gfx950): C ABI.
+ *
+ * The operation.  A row of S tokens holds one or more packs laid out as
+ * [prompt | response_0 | response_1 | ...] (the shared-prompt layout of
+ * "DPO Preference Packing: Dense Masks and Sparse Execution", section
+ * "Layout requirements"; K >= 2 responses after one prompt as in
+ * "Preference Packing", section 3.1).  Query i may attend key j when both
+ * lie in the same pack, j <= i, and j is a prompt token or lies in i's own
+ * response: each response sees the shared prompt and its own earlier
+ * tokens, never a sibling (same section), and nothing crosses a pack
+ * boundary, as with cumulative-sequence-length packing ("Why does packing
+ * several SFT examples into one sequence risk cross-example contamination?",
+ * "The correct implementation"; "Pack training sequences to reduce padding
+ * waste", the rule "same example AND key position <= query position").
+ * Attention itself is ordinary masked softmax attention; tiles of the
+ * score matrix that the mask empties are skipped, not computed
+ * ("DPO Preference Packing", section "Dense and sparse execution").
+ *
+ * Three calls:
+ *   pba_pack_block_map   descriptors -> per-token ids and windows, per-tile
+ *                        class (skip / partial / full) and visit lists
+ *   pba_packed_attn_fwd  Q, K, V (bf16, grouped heads) -> O (bf16), LSE (fp32)
+ *   pba_packed_attn_bwd  dO -> dQ, dK, dV (bf16)
+ *
+ * Conventions shared by every call.
+ *   - Every array argument is DEVICE memory allocated by the caller.  The
+ *     library never allocates, never synchronises, never keeps a pointer
+ *     after returning, and enqueues all work on `stream` (a hipStream_t;
+ *     NULL = the default stream).
+ *   - Host-visible argument errors return a negative PBA_ERR_* code and
+ *     enqueue nothing.  Errors in descriptor CONTENTS can only be seen on the
+ *     device: the map kernels record them in map->status (codes
+ *     PBA_DESC_*), and then the map kernels and any later fwd/bwd call that
+ *     uses that map write nothing.  Read map->status after a stream sync
+ *     to check.
+ *   - Layouts (row-major, contiguous): Q, O, dO, dQ [B, S, Hq, D];
+ *     K, V, dK, dV [B, S, Hkv, D]; LSE [B, Hq, S].  q head h uses kv head
+ *     h / (Hq / Hkv).  Pointers must be 16-byte aligned.
+ *   - Supported: D in {64, 128}; Hq % Hkv == 0; bf16 tensors; gfx950.
+ *   - Pad tokens (inside a row but in no pack) must hold finite values; they
+ *     never influence valid outputs and get O = 0, LSE = -inf and zero
+ *     gradients.
+ */
+#ifndef PBA_H
+#define PBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define PBA_API __attribute__((visibility("default")))
+#else
+#define PBA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes (host) ---------------------------------------------- */
+#define PBA_OK              0
+#define PBA_ERR_NULL       -1  /* a required pointer is NULL                      */
+#define PBA_ERR_SHAPE      -2  /* B, S, n_packs, n_resp_total or a head count out of range */
+#define PBA_ERR_HEADS      -3  /* Hq is not a multiple of Hkv                      */
+#define PBA_ERR_HEAD_DIM   -4  /* D not in {64, 128}                               */
+#define PBA_ERR_TILE       -5  /* tile shape unsupported, or map built for another tile shape */
+#define PBA_ERR_MAP        -6  /* map built for another (B, S), or its buffer too small */
+#define PBA_ERR_WORKSPACE  -7  /* backward workspace missing or too small           */
+#define PBA_ERR_DEVICE     -8  /* no gfx950 device current, or a HIP launch failed  */
+#define PBA_ERR_ALIGN      -9  /* a tensor pointer is not 16-byte aligned          */
+
+/* ---- device status codes (map->status[0]; status[1] = first bad pack) -- */
+#define PBA_DESC_OK          0
+#define PBA_DESC_ROW         1  /* row outside [0, B)                                 */
+#define PBA_DESC_NEGATIVE    2  /* negative start, prompt_len, n_resp or response length */
+#define PBA_DESC_RESP_RANGE  3  /* resp_first / n_resp outside resp_len[]              */
+#define PBA_DESC_BOUNDS      4  /* pack runs past the end of its row                   */
+#define PBA_DESC_ORDER       5  /* packs not sorted by (row, start), or overlapping    */
+
+/* ---- tile classes in map->cls ------------------------------------------ */
+#define PBA_TILE_SKIP     0
+#define PBA_TILE_PARTIAL  1
+#define PBA_TILE_FULL     2
+
+/* One pack: tokens [start, start + prompt_len + sum of its response lengths)
+ * of row `row`, prompt first, then responses resp_len[resp_first ..
+ * resp_first + n_resp - 1] in order.  The descriptor array is sorted by
+ * (row, start) with no overlaps; gaps between packs are pad.  A
+ * cumulative-sequence-length batch maps to row = 0, start = cu[p] and one
+ * response (or a prompt only) per pack.  Zero lengths are allowed. */
+typedef struct {
+  int32_t row;
+  int32_t start;
+  int32_t prompt_len;
+  int32_t n_resp;
+  int32_t resp_first;
+} pba_pack;
+
+/* The block map: a struct of device pointers into one caller-allocated
+ * buffer, filled in by pba_map_init and written by pba_pack_block_map.
+ * Tiles are block_m query tokens by block_n key tokens; nqt = ceil(S /
+ * block_m), nkt = ceil(S / block_n); tokens at or beyond S count as pad, so
+ * a tile touching them is never full.
+ *   tok_pack[b*S+s]    pack index covering token s of row b, -1 for pad
+ *   tok_branch[b*S+s]  0 in the prompt, k + 1 in response k, 0 for pad
+ *   tok_win[(b*S+s)*4 + {0,1,2,3}] = {kv_lo, pre_lo, pre_hi, q_end}:
+ *       as a query, token s sees keys [pre_lo, pre_hi) U [kv_lo, s]
+ *       (pre_lo = pre_hi = 0 when its visible keys form one run; kv_lo = s+1
+ *       for pad); as a key, it is seen by queries [s, q_end) (q_end = s for
+ *       pad).  Indices are positions within the row.
+ *   cls[(b*nqt+qt)*nkt+kt]     PBA_TILE_*
+ *   q2k_cnt[(b*nqt+qt)*2+{0,1}] = {n_full, n_partial} of query tile qt;
+ *   q2k_idx[(b*nqt+qt)*nkt + i] = its key tiles: full ones ascending, then
+ *       partial ones ascending, then -1.
+ *   k2q_cnt / k2q_idx: the same per key tile over query tiles ([B*nkt*2],
+ *       [B*nkt*nqt]).
+ *   totals[3] = {n_full, n_partial, n_skip} over all rows.
+ *   status[2] = {PBA_DESC_* code, first offending pack or -1}.            */
+typedef struct {
+  int32_t B, S, block_m, block_n, nqt, nkt;
+  int32_t* tok_pack;
+  int32_t* tok_branch;
+  int32_t* tok_win;
+  uint8_t* cls;
+  int32_t* q2k_cnt;
+  int32_t* q2k_idx;
+  int32_t* k2q_cnt;
+  int32_t* k2q_idx;
+  int64_t* totals;
+  int32_t* status;
+} pba_block_map;
+
+/* Error message for a return code or device status code (static string). */
+PBA_API const char* pba_strerror(int code);
+
+/* Tile shape (query tokens x key tokens) the forward / backward kernels need
+ * their map built with, for head dim D and the given head counts.  Returns
+ * PBA_OK or an argument error; *block_m / *block_n receive the shape. */
+PBA_API int pba_fwd_tile(int Hq, int Hkv, int D, int* block_m, int* block_n);
+PBA_API int pba_bwd_tile(int Hq, int Hkv, int D, int* block_m, int* block_n);
+
+/* Bytes of the single device buffer a map of this shape needs (0 on bad
+ * arguments).  Supported tiles: block_m, block_n in {16, 32, 64, 128, 256}. */
+PBA_API size_t pba_map_bytes(int B, int S, int block_m, int block_n);
+
+/* Point `map` into `buffer` (device memory, >= pba_map_bytes bytes, 256-byte
+ * aligned) for rows of S tokens.  Host only: enqueues nothing. */
+PBA_API int pba_map_init(pba_block_map* map, void* buffer, size_t buffer_bytes,
+                 int B, int S, int block_m, int block_n);
+
+/* Build the map from n_packs descriptors `packs` (device array of pba_pack)
+ * and n_resp_total response lengths `resp_len` (device int32).  Validates
+ * the descriptor contents on the device (map->status), then writes every
+ * other field of the map.  Asynchronous on `stream`. */
+PBA_API int pba_pack_block_map(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,
+                       const pba_block_map* map, void* stream);
+
+/* Forward.  For every query token and q head: O = softmax(scale * Q K^T
+ * restricted to the allowed keys) V, and LSE = natural log of the sum of
+ * exp(scale * q.k) over the allowed keys (the softmax normaliser, kept for
+ * the backward).  q, k, v, o: bf16 device arrays in the layouts above;
+ * lse: fp32 [B, Hq, S].  Only the map's full and partial tiles are
+ * computed; the mask is applied on partial tiles only.  The map must have
+ * been built for (B, S) with the tile shape of pba_fwd_tile. */
+PBA_API int pba_packed_attn_fwd(const pba_block_map* map, const void* q, const void* k, const void* v,
+                        void* o, float* lse, int B, int S, int Hq, int Hkv, int D,
+                        float softmax_scale, void* stream);
+
+/* Workspace bytes the backward needs (fp32 dQ accumulator and the per-row
+ * dot products rowsum(dO * O)); 0 on bad arguments. */
+PBA_API size_t pba_bwd_workspace_bytes(int B, int S, int Hq, int D);
+
+/* Backward of the forward above for the loss <dO, O>: dQ, dK, dV (bf16),
+ * with dK / dV summed over the q heads that share a kv head.  o and lse
+ * are the forward's outputs; dout is dO.  workspace: device memory of at
+ * least pba_bwd_workspace_bytes bytes, 256-byte aligned, contents
+ * irrelevant (overwritten).  The map must have been built for (B, S) with
+ * the tile shape of pba_bwd_tile. */
+PBA_API int pba_packed_attn_bwd(const pba_block_map* map, const void* q, const void* k, const void* v,
+                        const void* o, const float* lse, const void* dout,
+                        void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                        int B, int S, int Hq, int Hkv, int D, float softmax_scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PBA_H */

@@ -1,0 +1,78 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+host arguments synchronously (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "block_sparse_attention_pack_amd", "libpba.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from block_sparse_attention_pack_amd.build import build
+        build()
+    return ctypes.CDLL(LIB)
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "pba.h")).read()
+    return sorted(set(re.findall(r"PBA_API\s+[\w\s\*]+?\b(pba_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_three_calls():
+    names = _declared()
+    for n in ("pba_pack_block_map", "pba_packed_attn_fwd", "pba_packed_attn_bwd"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_binding_loads_and_lists_exports():
+    import block_sparse_attention_pack_amd as P
+    assert set(P.api.EXPORTED) == set(_declared())
+
+
+def test_host_argument_errors():
+    import block_sparse_attention_pack_amd as P
+    A = P.api
+    with pytest.raises(A.PbaError) as e:
+        A.fwd_tile(32, 7, 128)
+    assert e.value.code == -3
+    with pytest.raises(A.PbaError) as e:
+        A.fwd_tile(32, 8, 96)
+    assert e.value.code == -4
+    assert A.map_bytes(0, 10, 64, 64) == 0
+    assert A.map_bytes(1, 10, 48, 64) == 0
+    assert A.workspace_bytes(1, 10, 4, 80) == 0
+    assert A.fwd_tile(32, 8, 128) == (64, 64)
+    assert A.fwd_tile(4, 2, 64) == (128, 64)
+    assert A.fwd_tile(2, 2, 64) == (256, 64)
+    assert A.bwd_tile(32, 8, 128) == (64, 128)
+    lib = A._lib
+    # null map / null pointers are rejected before any device work
+    assert lib.pba_pack_block_map(None, 0, None, 0, None, None) == -1
+    assert lib.pba_packed_attn_fwd(None, 16, 16, 16, 16, 16, 1, 8, 2, 2, 64, 0.1, None) == -1
+    m = A.PbaBlockMap()
+    assert lib.pba_map_init(ctypes.byref(m), 256, 1 << 20, 2, 100, 64, 64) == 0
+    assert (m.nqt, m.nkt) == (2, 2)
+    assert lib.pba_map_init(ctypes.byref(m), 256 + 16, 1 << 20, 2, 100, 64, 64) == -9
+    assert lib.pba_map_init(ctypes.byref(m), 256, 16, 2, 100, 64, 64) == -6
+    # map shape mismatches are caught on the host
+    assert lib.pba_packed_attn_fwd(ctypes.byref(m), 16, 16, 16, 16, 16, 2, 101, 4, 2, 64, 0.1, None) == -6
+    assert lib.pba_packed_attn_fwd(ctypes.byref(m), 16, 16, 16, 16, 16, 2, 100, 4, 2, 64, 0.1, None) == -5
+    assert lib.pba_packed_attn_fwd(ctypes.byref(m), 16, 16, 16, 16, 16, 2, 100, 4, 3, 64, 0.1, None) == -3
+    assert lib.pba_packed_attn_fwd(ctypes.byref(m), 8, 16, 16, 16, 16, 2, 100, 4, 2, 64, 0.1, None) == -9
+    ws = A.workspace_bytes(2, 100, 4, 64)
+    assert ws >= 2 * 100 * 4 * 64 * 4 + 2 * 4 * 100 * 4
+    mb = A.PbaBlockMap()
+    assert lib.pba_map_init(ctypes.byref(mb), 256, 1 << 20, 2, 100, 64, 128) == 0
+    args = [ctypes.byref(mb)] + [16] * 10
+    assert lib.pba_packed_attn_bwd(*args[:10], 256, 0, 2, 100, 4, 2, 64, 0.1, None) == -7
+    assert lib.pba_packed_attn_bwd(*args[:10], 256, ws - 1, 2, 100, 4, 2, 64, 0.1, None) == -7

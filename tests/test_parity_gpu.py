@@ -1,0 +1,157 @@
+"""HIP forward / backward vs the fp64 oracle.
+
+Acceptance: O max-abs <= 1e-2 and rel-L2 <= 1e-2; LSE abs <= 1e-3 on valid
+rows; dQ, dK, dV rel-L2 <= 1e-2; pad rows O = 0, LSE = -inf, zero grads.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_path import api, rel_l2, run_fwd_bwd, say
+from workloads.generate import Pack, PackSet, descriptor_arrays, make_workload, random_packset
+
+pytestmark = pytest.mark.gpu
+
+O_ABS, O_REL, LSE_ABS, G_REL = 1e-2, 1e-2, 1e-3, 1e-2
+
+
+def _mask(ps):
+    P, R = descriptor_arrays(ps)
+    pk, br, st = oracle.token_ids(P, R, ps.B, ps.S)
+    assert tuple(st) == (0, -1)
+    return oracle.attention_mask(pk, br), pk
+
+
+def _check_full(w, got, tag):
+    m, pk = _mask(w.packset)
+    O, L = oracle.attn_fwd(w.q, w.k, w.v, m, w.scale)
+    dq, dk, dv = oracle.attn_bwd(w.q, w.k, w.v, w.do, m, w.scale)
+    valid = torch.from_numpy(pk >= 0)                      # [B, S]
+    vq = valid[:, :, None, None]
+    o = got["o"].to(torch.float64)
+    assert float((o - O).abs().max()) <= O_ABS, tag
+    assert rel_l2(o[valid], O[valid]) <= O_REL, (tag, rel_l2(o[valid], O[valid]))
+    lse = got["lse"].to(torch.float64)
+    vl = valid[:, None, :].expand_as(lse)
+    assert float((lse[vl] - L[vl]).abs().max()) <= LSE_ABS, tag
+    assert torch.isneginf(lse[~vl]).all(), tag
+    assert (o[~valid] == 0).all(), tag
+    for name, x, ref in (("dq", got["dq"], dq), ("dk", got["dk"], dk), ("dv", got["dv"], dv)):
+        x = x.to(torch.float64)
+        e = rel_l2(x[valid], ref[valid])
+        assert e <= G_REL, (tag, name, e)
+        assert (x[~valid] == 0).all(), (tag, name)
+    return True
+
+
+def test_tiny_config():
+    say("parity tiny")
+    w = make_workload(1)
+    _check_full(w, run_fwd_bwd(w), "tiny")
+
+
+@pytest.mark.parametrize("heads", [(4, 2, 64), (8, 1, 128), (4, 4, 128), (2, 2, 64), (8, 2, 128), (32, 8, 128)])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_random_ragged_packs(heads, seed):
+    rng = np.random.default_rng(2000 + seed)
+    S = int(rng.integers(150, 420))
+    ps = random_packset(rng, B=2, S=S, max_packs_per_row=3, max_resp=4, max_len=120)
+    if not ps.packs:
+        ps = PackSet(2, S, [Pack(0, 0, 10, (20,))])
+    w = make_workload(None, seed, packset=ps, heads=heads)
+    say("parity random", heads, seed, ps.B, ps.S, len(ps.packs))
+    _check_full(w, run_fwd_bwd(w), f"random {heads} {seed}")
+
+
+def test_unscaled_multi_tile():
+    ps = PackSet(2, 600, [Pack(0, 0, 200, (150, 170)), Pack(0, 520, 30, (40,)), Pack(1, 7, 64, (128, 64, 1, 200))])
+    w = make_workload(None, 3, packset=ps, heads=(8, 2, 128))
+    say("parity unscaled multi-tile")
+    _check_full(w, run_fwd_bwd(w), "multi")
+
+
+def test_pad_inertness():
+    """Changing pad-token values changes no valid output bit."""
+    ps = PackSet(1, 300, [Pack(0, 5, 100, (50, 60)), Pack(0, 230, 20, (30,))])
+    w = make_workload(None, 4, packset=ps, heads=(4, 2, 128))
+    a = run_fwd_bwd(w)
+    _, pk = _mask(ps)
+    pad = torch.from_numpy(pk < 0)[0]
+    for x in (w.q, w.k, w.v, w.do):
+        x[0, pad] = torch.randn_like(x[0, pad], dtype=torch.float32).to(torch.bfloat16) * 7
+    b = run_fwd_bwd(w)
+    for f in ("o", "lse", "dq", "dk", "dv"):
+        assert torch.equal(a[f], b[f]), f
+
+
+def test_negative_control_corrupted_map_fails():
+    """Relabelling one partial tile as full (so its mask is skipped) must
+    break parity: the check above can fail."""
+    w = make_workload(1)
+    A = api()
+    from gpu_path import build_map
+    dev = "cuda"
+    q, k, v = (x.to(dev) for x in (w.q, w.k, w.v))
+    fm = build_map(w.packset, *A.fwd_tile(w.Hq, w.Hkv, w.D))
+    cnt = fm.q2k_cnt()
+    c = cnt.cpu()
+    qt = int(torch.nonzero(c[0, :, 1] > 0)[0])
+    cnt[0, qt, 0] += 1
+    cnt[0, qt, 1] -= 1
+    o, lse = A.packed_attn_fwd(fm, q, k, v, w.scale)
+    m, pk = _mask(w.packset)
+    O, L = oracle.attn_fwd(w.q, w.k, w.v, m, w.scale)
+    valid = torch.from_numpy(pk >= 0)
+    err = float((o.cpu().double() - O).abs()[valid].max())
+    say("negative control error", err)
+    assert err > O_ABS
+
+
+def _sample_rows(rng, pk_b, n):
+    idx = np.flatnonzero(pk_b >= 0)
+    pick = rng.choice(idx, size=min(n, len(idx)), replace=False)
+    # always include the first and last token of every run boundary region
+    return np.sort(pick)
+
+
+@pytest.mark.parametrize("cfg,unscaled", [(2, False), (2, True), (3, False), (4, False), (5, False),
+                                          (3, True), (4, True), (5, True), ("3alt", False)])
+def test_full_size_sampled(cfg, unscaled):
+    w = make_workload(cfg, 0, unscaled=unscaled)
+    say("parity full-size", cfg, "unscaled" if unscaled else "scaled", w.packset.B, w.packset.S)
+    got = run_fwd_bwd(w)
+    P, R = descriptor_arrays(w.packset)
+    pk, br, _ = oracle.token_ids(P, R, w.packset.B, w.packset.S)
+    rng = np.random.default_rng(7)
+    B = w.packset.B
+    # forward: sampled rows of sampled heads, every batch row
+    for b in range(B):
+        mb = oracle.attention_mask(pk, br, row=b)
+        rows = _sample_rows(rng, pk[b], 48)
+        for h in rng.choice(w.Hq, size=3, replace=False):
+            Os, Ls = oracle.attn_fwd_rows(w.q, w.k, w.v, mb, b, int(h), rows, w.scale)
+            o = got["o"][b, rows, int(h)].double()
+            assert float((o - Os).abs().max()) <= O_ABS
+            assert rel_l2(o, Os) <= O_REL, rel_l2(o, Os)
+            assert float((got["lse"][b, int(h), rows].double() - Ls).abs().max()) <= LSE_ABS
+        pad = pk[b] < 0
+        if pad.any():
+            assert (got["o"][b, torch.from_numpy(pad)] == 0).all()
+            assert torch.isneginf(got["lse"][b][:, torch.from_numpy(pad)]).all()
+    # backward: one (row, kv head) pair, sampled query rows and keys
+    b = int(rng.integers(0, B))
+    g = int(rng.integers(0, w.Hkv))
+    mb = oracle.attention_mask(pk, br, row=b)
+    qrows = _sample_rows(rng, pk[b], 64)
+    krows = _sample_rows(rng, pk[b], 64)
+    dqs, dks, dvs = oracle.attn_bwd_sampled(w.q, w.k, w.v, w.do, mb, b, g, qrows, krows, w.scale)
+    G = w.Hq // w.Hkv
+    dq = torch.stack([got["dq"][b, qrows, h] for h in range(g * G, (g + 1) * G)]).double()
+    for name, x, ref in (("dq", dq, dqs), ("dk", got["dk"][b, krows, g].double(), dks),
+                         ("dv", got["dv"][b, krows, g].double(), dvs)):
+        e = rel_l2(x, ref)
+        say(" ", name, "rel-L2", e)
+        assert e <= G_REL, (name, e)
