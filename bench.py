@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Throughput of packed branch-aware attention (fwd + bwd) on one MI355X.
+
+One step = the whole hot path over one batch: build the forward and backward
+block maps from the pack descriptors, the forward kernel, then the three
+backward stages (rowsum(dO*O) pass, main kernel, dQ convert).  Inputs are
+resident in HBM before timing; outputs, maps and workspace are preallocated.
+
+Metric: useful TFLOP/s = 14 * D * Hq * (allowed query-key pairs) per step /
+step time (4*D forward + 10*D backward per allowed pair and q head; masked
+pairs and skipped tiles earn nothing), also as a fraction of the bf16 MFMA
+peak.  Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--config 2]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12   # 2516.6: 256 CUs x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense)
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse_cfg(s):
+    return s if s == "3alt" else int(s)
+
+
+class Runner:
+    """Preallocated buffers for one workload; step() enqueues the hot path."""
+
+    def __init__(self, A, torch, ps, q, k, v, do, Hq, Hkv, D, scale, dense=False):
+        from workloads.generate import descriptor_arrays
+        self.A, self.torch = A, torch
+        self.ps, self.Hq, self.Hkv, self.D, self.scale = ps, Hq, Hkv, D, scale
+        P, R = descriptor_arrays(ps)
+        self.P, self.R = A.descriptors_to_device(P, R)
+        self.n_packs, self.n_resp = P.shape[0], R.shape[0]
+        self.ftile, self.btile = A.fwd_tile(Hq, Hkv, D), A.bwd_tile(Hq, Hkv, D)
+        self.fmap = A.BlockMap(ps.B, ps.S, *self.ftile)
+        self.bmap = A.BlockMap(ps.B, ps.S, *self.btile)
+        self.q, self.k, self.v, self.do = q, k, v, do
+        self.o = torch.empty_like(q)
+        self.lse = torch.empty((ps.B, Hq, ps.S), dtype=torch.float32, device=q.device)
+        self.dq, self.dk, self.dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        self.ws = torch.empty(A.workspace_bytes(ps.B, ps.S, Hq, D) + 256, dtype=torch.uint8, device=q.device)
+        self.dense = dense
+        if dense:
+            self.build_maps()
+            for m in (self.fmap, self.bmap):
+                self._densify(m)
+            torch.cuda.synchronize()
+
+    def _densify(self, m):
+        """Every tile pair visited and masked: the dense packed baseline."""
+        t = self.torch
+        m.q2k_cnt()[:, :, 0] = 0
+        m.q2k_cnt()[:, :, 1] = m.nkt
+        m.q2k_idx().copy_(t.arange(m.nkt, dtype=t.int32, device="cuda").expand(m.B, m.nqt, m.nkt))
+        m.k2q_cnt()[:, :, 0] = 0
+        m.k2q_cnt()[:, :, 1] = m.nqt
+        m.k2q_idx().copy_(t.arange(m.nqt, dtype=t.int32, device="cuda").expand(m.B, m.nkt, m.nqt))
+
+    def build_maps(self):
+        A, ps = self.A, self.ps
+        A.pack_block_map(self.P, self.R, ps.B, ps.S, *self.ftile, out=self.fmap)
+        A.pack_block_map(self.P, self.R, ps.B, ps.S, *self.btile, out=self.bmap)
+
+    def fwd(self):
+        self.A.packed_attn_fwd(self.fmap, self.q, self.k, self.v, self.scale, out=(self.o, self.lse))
+
+    def bwd(self, stages):
+        self.A.packed_attn_bwd(self.bmap, self.q, self.k, self.v, self.o, self.lse, self.do, self.scale,
+                               out=(self.dq, self.dk, self.dv), workspace=self.ws, stages=stages)
+
+    def step(self, ev=None):
+        A = self.A
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        if not self.dense:
+            self.build_maps()
+        rec(1)
+        self.fwd()
+        rec(2)
+        self.bwd(A.BWD_PREPROCESS)
+        rec(3)
+        self.bwd(A.BWD_MAIN)
+        rec(4)
+        self.bwd(A.BWD_FINALIZE)
+        rec(5)
+
+
+def time_runner(torch, r, steps, warmup):
+    for _ in range(warmup):
+        r.step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        r.step(evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    names = ["map", "fwd", "bwd_pre", "bwd_main", "bwd_fin"]
+    per = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps for i, n in enumerate(names)}
+    per["step_events"] = sum(e[0].elapsed_time(e[5]) for e in evs) / steps
+    return wall * 1e3, per
+
+
+def allowed_pairs(ps):
+    n = 0
+    for p in ps.packs:
+        n += p.prompt_len * (p.prompt_len + 1) // 2
+        for r in p.resp_lens:
+            n += r * p.prompt_len + r * (r + 1) // 2
+    return n
+
+
+def map_bytes(r, m):
+    B, S = r.ps.B, r.ps.S
+    return (20 * r.n_packs + 4 * r.n_resp + 24 * B * S + 9 * B * m.nqt * m.nkt + 8 * B * (m.nqt + m.nkt))
+
+
+def traffic_record(kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "block_sparse_attention_pack_amd", "csrc", rec["source"])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if sha != rec.get("source_sha256"):
+        return None
+    return rec
+
+
+def cpu_baseline(w, seconds):
+    """The fp64 oracle (dense masked attention + naive backward) on a bounded
+    sample of the same workload: whole (batch row, kv group) units, in order,
+    until `seconds` of wall time have been spent."""
+    import torch
+    import oracle
+    from workloads.generate import descriptor_arrays
+    cores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(cores)
+    ps = w.packset
+    P, R = descriptor_arrays(ps)
+    pk, br, _ = oracle.token_ids(P, R, ps.B, ps.S)
+    G = w.Hq // w.Hkv
+    flops, units, t_used = 0.0, [], 0.0
+    for b in range(ps.B):
+        mb = oracle.attention_mask(pk, br, row=b)
+        n_allowed = int(mb.sum())
+        for g in range(w.Hkv):
+            t0 = time.perf_counter()
+            rowmask = _RowMask(mb, b)
+            oracle.attn_fwd(w.q, w.k, w.v, rowmask, w.scale, rows=[b], heads=range(g * G, (g + 1) * G))
+            oracle.attn_bwd(w.q, w.k, w.v, w.do, rowmask, w.scale, rows=[b], groups=[g])
+            t_used += time.perf_counter() - t0
+            flops += 14.0 * w.D * G * n_allowed
+            units.append((b, g))
+            if t_used >= seconds:
+                break
+        if t_used >= seconds:
+            break
+    cpu = platform.processor() or platform.machine()
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"fp64 oracle fwd+bwd on {len(units)} of {ps.B * w.Hkv} (batch row, kv group) units "
+                      f"({G} q heads each) of the same workload, {t_used:.1f} s wall, useful-FLOP rate; CPU: {cpu}"}
+
+
+class _RowMask:
+    """Indexable stand-in for a [B, S, S] mask that holds one row's mask."""
+
+    def __init__(self, mb, b):
+        self.mb, self.b = mb, b
+
+    def __getitem__(self, i):
+        assert i == self.b
+        return self.mb
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="2", help="workload 1..5 or 3alt (default 2: Qwen3-8B-shaped packs)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-baselines", action="store_true", help="skip the dense-map and pairwise-layout runs")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path (packs and kv-head groups "
+              "shard with no exchange; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from workloads.generate import make_workload, pairwise_packset, pairwise_tensors
+    import block_sparse_attention_pack_amd as pkg
+    A = pkg.api
+
+    cfg = parse_cfg(args.config)
+    w = make_workload(cfg, 0)
+    ps = w.packset
+    dev = torch.device("cuda:0")
+    q, k, v, do = (x.to(dev).contiguous() for x in (w.q, w.k, w.v, w.do))
+    torch.cuda.synchronize()
+    n_allowed = allowed_pairs(ps)
+    useful = 14.0 * w.D * w.Hq * n_allowed
+    log(f"workload {w.name}: B={ps.B} S={ps.S} Hq={w.Hq} Hkv={w.Hkv} D={w.D} allowed={n_allowed} "
+        f"useful={useful:.3e} FLOP/step")
+
+    r = Runner(A, torch, ps, q, k, v, do, w.Hq, w.Hkv, w.D, w.scale)
+    ms, per = time_runner(torch, r, args.steps, args.warmup)
+    tot = r.fmap.totals().cpu().tolist()
+    totb = r.bmap.totals().cpu().tolist()
+    value = useful / (ms * 1e-3) / 1e12
+    log(f"step {ms:.3f} ms  useful {value:.1f} TFLOP/s  per-kernel ms {json.dumps({k_: round(v_, 4) for k_, v_ in per.items()})}")
+
+    fwd_flops, bwd_flops = 4.0 * w.D * w.Hq * n_allowed, 10.0 * w.D * w.Hq * n_allowed
+    kern = {
+        "fwd": {"ms": per["fwd"], "useful_tflops": fwd_flops / (per["fwd"] * 1e-3) / 1e12},
+        "bwd_main": {"ms": per["bwd_main"], "useful_tflops": bwd_flops / (per["bwd_main"] * 1e-3) / 1e12},
+        "map": {"ms": per["map"], "GBps": (map_bytes(r, r.fmap) + map_bytes(r, r.bmap)) / (per["map"] * 1e-3) / 1e9},
+        "bwd_pre": {"ms": per["bwd_pre"],
+                    "GBps": ps.B * ps.S * w.Hq * (8.0 * w.D + 4) / (per["bwd_pre"] * 1e-3) / 1e9},
+        "bwd_fin": {"ms": per["bwd_fin"], "GBps": ps.B * ps.S * w.Hq * 6.0 * w.D / (per["bwd_fin"] * 1e-3) / 1e9},
+    }
+    dom = "bwd_main" if per["bwd_main"] >= per["fwd"] else "fwd"
+    achieved = kern[dom]["useful_tflops"]
+    tr = traffic_record(dom)
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": (tr["hbm_bytes_per_launch"] if tr else None)}
+
+    extra = {"skip_frac_fwd_tiles": tot[2] / max(1, sum(tot)), "tiles_fwd": {"full": tot[0], "partial": tot[1], "skip": tot[2],
+             "shape": list(r.ftile)},
+             "skip_frac_bwd_tiles": totb[2] / max(1, sum(totb)), "tiles_bwd": {"full": totb[0], "partial": totb[1],
+             "skip": totb[2], "shape": list(r.btile)},
+             "kernels": kern, "frac_of_peak": value / PEAK_BF16_TFLOPS, "allowed_pairs": n_allowed,
+             "useful_flop_per_step": useful, "step_ms_events": per["step_events"]}
+
+    if not args.no_baselines:
+        rd = Runner(A, torch, ps, q, k, v, do, w.Hq, w.Hkv, w.D, w.scale, dense=True)
+        ms_d, per_d = time_runner(torch, rd, args.steps, args.warmup)
+        att = lambda p: p["fwd"] + p["bwd_pre"] + p["bwd_main"] + p["bwd_fin"]  # noqa: E731
+        del rd
+        pps, pairs = pairwise_packset(ps)
+        pt = [pairwise_tensors(x, pairs, pps.S).to(dev).contiguous() for x in (w.q, w.k, w.v, w.do)]
+        rp = Runner(A, torch, pps, *pt, w.Hq, w.Hkv, w.D, w.scale)
+        ms_p, per_p = time_runner(torch, rp, args.steps, args.warmup)
+        del rp, pt
+        extra.update({
+            "attn_ms_sparse": att(per), "attn_ms_dense_map": att(per_d), "attn_ms_pairwise": att(per_p),
+            "speedup_vs_dense_packed": att(per_d) / att(per),
+            "speedup_vs_pairwise": att(per_p) / att(per),
+            "pairwise_layout": {"B": pps.B, "S": pps.S, "allowed_pairs": allowed_pairs(pps)},
+        })
+        log(f"dense-map attn {att(per_d):.3f} ms, pairwise attn {att(per_p):.3f} ms, sparse attn {att(per):.3f} ms")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host ...")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        log(f"cpu baseline {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": "useful TFLOP/s packed-attention fwd+bwd (unmasked FLOPs); % bf16 MFMA peak",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded lognormal pack lengths standing in for UltraFeedback-style preference data)",
+        "config": {"workload": w.name, "batch": ps.B, "seq_len": ps.S, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.D, "packs": len(ps.packs), "real_tokens": ps.real_tokens()},
+        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

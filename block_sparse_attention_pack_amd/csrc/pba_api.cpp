@@ -223,10 +223,11 @@ size_t pba_bwd_workspace_bytes(int B, int S, int Hq, int D) {
   return align_up((size_t)B * S * Hq * D * 4) + align_up((size_t)B * Hq * S * 4);
 }
 
-int pba_packed_attn_bwd(const pba_block_map* map, const void* q, const void* k, const void* v, const void* o,
-                        const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
-                        size_t workspace_bytes, int B, int S, int Hq, int Hkv, int D, float softmax_scale,
-                        void* stream) {
+int pba_packed_attn_bwd_stages(int stages, const pba_block_map* map, const void* q, const void* k, const void* v,
+                               const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, int B, int S, int Hq, int Hkv, int D,
+                               float softmax_scale, void* stream) {
+  if (stages < 1 || stages > PBA_BWD_ALL) return PBA_ERR_SHAPE;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return PBA_ERR_NULL;
   if (int rc = check_heads(B, S, Hq, Hkv, D)) return rc;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
@@ -259,8 +260,16 @@ int pba_packed_attn_bwd(const pba_block_map* map, const void* q, const void* k, 
   a.G = Hq / Hkv;
   a.scale = softmax_scale;
   a.scale_log2 = softmax_scale * pba::kLog2eHost;
-  hipError_t e = pba::launch_bwd(a, D, static_cast<hipStream_t>(stream));
+  hipError_t e = pba::launch_bwd(a, D, stages, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PBA_OK : PBA_ERR_DEVICE;
+}
+
+int pba_packed_attn_bwd(const pba_block_map* map, const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                        size_t workspace_bytes, int B, int S, int Hq, int Hkv, int D, float softmax_scale,
+                        void* stream) {
+  return pba_packed_attn_bwd_stages(PBA_BWD_ALL, map, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
+                                    B, S, Hq, Hkv, D, softmax_scale, stream);
 }
 
 }  // extern "C"

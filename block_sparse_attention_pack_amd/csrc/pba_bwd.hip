@@ -306,19 +306,20 @@ __global__ void __launch_bounds__(256, 1) bwd_main(BwdArgs a) {
 }
 
 template <int D>
-hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_bwd_stage_d(const BwdArgs& a, int stage, hipStream_t stream) {
   const int64_t nchunks = (int64_t)a.B * a.S * a.Hq * D / 8;
   const unsigned nb = (unsigned)((nchunks + 255) / 256);
-  bwd_delta<D><<<nb, 256, 0, stream>>>(a.o, a.dout, a.delta, a.dq_acc, nchunks, a.S, a.Hq, a.map.status);
-  bwd_main<D><<<dim3(a.map.nkt, a.Hkv, a.B), 256, 0, stream>>>(a);
-  bwd_dq_cvt<<<nb, 256, 0, stream>>>(a.dq_acc, a.dq, nchunks, a.map.status);
+  if (stage & kBwdPre)
+    bwd_delta<D><<<nb, 256, 0, stream>>>(a.o, a.dout, a.delta, a.dq_acc, nchunks, a.S, a.Hq, a.map.status);
+  if (stage & kBwdMain) bwd_main<D><<<dim3(a.map.nkt, a.Hkv, a.B), 256, 0, stream>>>(a);
+  if (stage & kBwdFin) bwd_dq_cvt<<<nb, 256, 0, stream>>>(a.dq_acc, a.dq, nchunks, a.map.status);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& a, int D, hipStream_t stream) {
-  return D == 128 ? launch_bwd_d<128>(a, stream) : launch_bwd_d<64>(a, stream);
+hipError_t launch_bwd(const BwdArgs& a, int D, int stages, hipStream_t stream) {
+  return D == 128 ? launch_bwd_stage_d<128>(a, stages, stream) : launch_bwd_stage_d<64>(a, stages, stream);
 }
 
 }  // namespace pba

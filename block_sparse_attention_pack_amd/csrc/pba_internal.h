@@ -67,6 +67,8 @@ constexpr float kLog2eHost = 1.4426950408889634f;
 hipError_t launch_map(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,
                       const pba_block_map& map, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int D, int B, hipStream_t stream);
-hipError_t launch_bwd(const BwdArgs& a, int D, hipStream_t stream);
+// Backward stages (bit mask): delta + accumulator clear, main, dQ convert.
+constexpr int kBwdPre = 1, kBwdMain = 2, kBwdFin = 4, kBwdAll = 7;
+hipError_t launch_bwd(const BwdArgs& a, int D, int stages, hipStream_t stream);
 
 }  // namespace pba

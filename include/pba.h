@@ -182,6 +182,25 @@ PBA_API int pba_packed_attn_bwd(const pba_block_map* map, const void* q, const v
                         void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                         int B, int S, int Hq, int Hkv, int D, float softmax_scale, void* stream);
 
+/* The backward in its three stages, for callers that schedule or time them
+ * separately.  `stages` is a bit mask; running all three in order on one
+ * stream is exactly pba_packed_attn_bwd:
+ *   PBA_BWD_PREPROCESS  workspace <- rowsum(dO * O) per (row, q head, token),
+ *                       and the fp32 dQ accumulator <- 0
+ *   PBA_BWD_MAIN        dK, dV written; scale * dS K added into the dQ
+ *                       accumulator (needs the preprocess stage's workspace)
+ *   PBA_BWD_FINALIZE    dQ <- bf16(dQ accumulator)
+ * Arguments as for pba_packed_attn_bwd (all are checked for every stage);
+ * returns PBA_ERR_SHAPE for an empty or unknown mask. */
+#define PBA_BWD_PREPROCESS 1
+#define PBA_BWD_MAIN       2
+#define PBA_BWD_FINALIZE   4
+#define PBA_BWD_ALL        7
+PBA_API int pba_packed_attn_bwd_stages(int stages, const pba_block_map* map, const void* q, const void* k,
+                                       const void* v, const void* o, const float* lse, const void* dout,
+                                       void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                                       int B, int S, int Hq, int Hkv, int D, float softmax_scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
