@@ -36,7 +36,8 @@ class PbaBlockMap(ctypes.Structure):
         ("tok_pack", ctypes.c_void_p), ("tok_branch", ctypes.c_void_p), ("tok_win", ctypes.c_void_p),
         ("cls", ctypes.c_void_p), ("q2k_cnt", ctypes.c_void_p), ("q2k_idx", ctypes.c_void_p),
         ("k2q_cnt", ctypes.c_void_p), ("k2q_idx", ctypes.c_void_p), ("totals", ctypes.c_void_p),
-        ("status", ctypes.c_void_p),
+        ("status", ctypes.c_void_p), ("q_order", ctypes.c_void_p), ("k_order", ctypes.c_void_p),
+        ("work", ctypes.c_void_p),
     ]
 
 
@@ -159,6 +160,12 @@ class BlockMap:
     def status(self):
         return self._view("status", 2, torch.int32)
 
+    def q_order(self):
+        return self._view("q_order", self.B * self.nqt, torch.int32)
+
+    def k_order(self):
+        return self._view("k_order", self.B * self.nkt, torch.int32)
+
     def to_host(self) -> dict:
         """Every field as numpy (synchronises)."""
         return {
@@ -169,6 +176,7 @@ class BlockMap:
             "q2k_cnt": self.q2k_cnt().cpu().numpy(), "q2k_idx": self.q2k_idx().cpu().numpy(),
             "k2q_cnt": self.k2q_cnt().cpu().numpy(), "k2q_idx": self.k2q_idx().cpu().numpy(),
             "totals": self.totals().cpu().numpy(), "status": self.status().cpu().numpy(),
+            "q_order": self.q_order().cpu().numpy(), "k_order": self.k_order().cpu().numpy(),
         }
 
 

@@ -27,14 +27,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 // Field sizes of a map, in the order they are carved from the buffer.
 struct MapLayout {
-  size_t off[10];
+  size_t off[13];
   size_t total;
 };
 
 MapLayout map_layout(int B, int S, int bm, int bn) {
   const size_t nqt = (size_t)((S + bm - 1) / bm), nkt = (size_t)((S + bn - 1) / bn);
   const size_t ntok = (size_t)B * S;
-  const size_t sizes[10] = {
+  const size_t sizes[13] = {
       4 * ntok,               // tok_pack
       4 * ntok,               // tok_branch
       16 * ntok,              // tok_win
@@ -45,10 +45,13 @@ MapLayout map_layout(int B, int S, int bm, int bn) {
       4 * (size_t)B * nkt * nqt,  // k2q_idx
       3 * 8,                  // totals
       2 * 4,                  // status
+      4 * (size_t)B * nqt,    // q_order
+      4 * (size_t)B * nkt,    // k_order
+      4 * (nqt + nkt + 2),    // work (order histograms)
   };
   MapLayout L;
   size_t o = 0;
-  for (int i = 0; i < 10; ++i) {
+  for (int i = 0; i < 13; ++i) {
     L.off[i] = o;
     o += align_up(sizes[i]);
   }
@@ -77,7 +80,9 @@ int device_ok() {
 }
 
 int check_map(const pba_block_map* m, int B, int S, int bm, int bn) {
-  if (!m || !m->tok_win || !m->q2k_cnt || !m->q2k_idx || !m->k2q_cnt || !m->k2q_idx || !m->status) return PBA_ERR_NULL;
+  if (!m || !m->tok_win || !m->q2k_cnt || !m->q2k_idx || !m->k2q_cnt || !m->k2q_idx || !m->status || !m->q_order ||
+      !m->k_order)
+    return PBA_ERR_NULL;
   if (m->B != B || m->S != S) return PBA_ERR_MAP;
   if (m->block_m != bm || m->block_n != bn) return PBA_ERR_TILE;
   if (m->nqt != (S + bm - 1) / bm || m->nkt != (S + bn - 1) / bn) return PBA_ERR_MAP;
@@ -96,6 +101,7 @@ pba::MapView view_of(const pba_block_map* m) {
   v.B = m->B; v.S = m->S; v.bm = m->block_m; v.bn = m->block_n; v.nqt = m->nqt; v.nkt = m->nkt;
   v.tok_win = m->tok_win; v.q2k_cnt = m->q2k_cnt; v.q2k_idx = m->q2k_idx;
   v.k2q_cnt = m->k2q_cnt; v.k2q_idx = m->k2q_idx; v.status = m->status;
+  v.q_order = m->q_order; v.k_order = m->k_order;
   return v;
 }
 
@@ -173,13 +179,16 @@ int pba_map_init(pba_block_map* map, void* buffer, size_t buffer_bytes, int B, i
   map->k2q_idx = reinterpret_cast<int32_t*>(base + L.off[7]);
   map->totals = reinterpret_cast<int64_t*>(base + L.off[8]);
   map->status = reinterpret_cast<int32_t*>(base + L.off[9]);
+  map->q_order = reinterpret_cast<int32_t*>(base + L.off[10]);
+  map->k_order = reinterpret_cast<int32_t*>(base + L.off[11]);
+  map->work = reinterpret_cast<int32_t*>(base + L.off[12]);
   return PBA_OK;
 }
 
 int pba_pack_block_map(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,
                        const pba_block_map* map, void* stream) {
   if (!map || !map->tok_pack || !map->tok_branch || !map->tok_win || !map->cls || !map->q2k_cnt || !map->q2k_idx ||
-      !map->k2q_cnt || !map->k2q_idx || !map->totals || !map->status)
+      !map->k2q_cnt || !map->k2q_idx || !map->totals || !map->status || !map->q_order || !map->k_order || !map->work)
     return PBA_ERR_NULL;
   if (n_packs < 0 || n_resp_total < 0) return PBA_ERR_SHAPE;
   if ((n_packs > 0 && !packs) || (n_resp_total > 0 && !resp_len)) return PBA_ERR_NULL;

@@ -14,11 +14,12 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 #define PBA_LDS __attribute__((address_space(3)))
 
 // Tile shapes of the attention kernels (query tokens x key tokens).
-constexpr int kFwdBM = 64;   // one wave owns 64 query rows of one q head
+constexpr int kFwdBM = 32;   // one wave owns 32 query rows of one q head
 constexpr int kFwdBN = 64;
 constexpr int kBwdBM = 64;   // query rows per backward step
 constexpr int kBwdBN = 128;  // key rows per backward workgroup (4 waves x 32)
@@ -31,6 +32,8 @@ struct MapView {  // device-side view of a pba_block_map
   const int32_t* k2q_cnt;
   const int32_t* k2q_idx;
   const int32_t* status;
+  const int32_t* q_order;  // [B*nqt] query tiles, longest visit list first
+  const int32_t* k_order;  // [B*nkt] key tiles, longest visit list first
 };
 
 struct FwdArgs {

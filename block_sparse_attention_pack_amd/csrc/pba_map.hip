@@ -213,6 +213,82 @@ __global__ void __launch_bounds__(kThreads) map_lists(const uint8_t* __restrict_
   }
 }
 
+
+// One block per order array (block 0: query tiles, block 1: key tiles).
+// Stable counting sort by visit count, descending: a histogram of the
+// counts, its exclusive scan from the largest count down (bucket starts),
+// then placement in index order, one chunk of kThreads items at a time,
+// each item going after the earlier items of its bucket.  The histogram
+// lives in map->work and is accessed with device-scope atomics only, so
+// every phase sees the previous one's values in L2.
+__global__ void __launch_bounds__(kThreads) map_order(int B, int nqt, int nkt, const int32_t* __restrict__ status,
+                                                      const int32_t* __restrict__ q2k_cnt,
+                                                      const int32_t* __restrict__ k2q_cnt, int32_t* q_order,
+                                                      int32_t* k_order, int32_t* work) {
+  if (status[0] != 0) return;
+  __shared__ int s_c[kThreads];
+  __shared__ int s_sum[kThreads];
+  const int tid = threadIdx.x;
+  const bool qside = blockIdx.x == 0;
+  const int n = qside ? B * nqt : B * nkt;
+  const int maxc = qside ? nkt : nqt;
+  const int32_t* cnt = qside ? q2k_cnt : k2q_cnt;
+  int32_t* order = qside ? q_order : k_order;
+  int32_t* hist = work + (qside ? 0 : nkt + 1);
+  auto ld = [](int32_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  auto st = [](int32_t* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  auto count_of = [&](int i) { return min(max(cnt[2 * i] + cnt[2 * i + 1], 0), maxc); };
+
+  for (int c = tid; c <= maxc; c += kThreads) st(hist + c, 0);
+  __threadfence();
+  __syncthreads();
+  for (int i = tid; i < n; i += kThreads) atomicAdd(hist + count_of(i), 1);
+  __threadfence();
+  __syncthreads();
+  // Bucket starts: start[c] = number of items with a larger count.
+  int running = 0;
+  for (int top = maxc; top >= 0; top -= kThreads) {
+    const int c = top - tid;
+    const int v = c >= 0 ? ld(hist + c) : 0;
+    s_sum[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {  // inclusive scan over tid
+      const int x = tid >= off ? s_sum[tid - off] : 0;
+      __syncthreads();
+      s_sum[tid] += x;
+      __syncthreads();
+    }
+    if (c >= 0) st(hist + c, running + s_sum[tid] - v);
+    running += s_sum[kThreads - 1];
+    __syncthreads();
+  }
+  __threadfence();
+  __syncthreads();
+  for (int base = 0; base < n; base += kThreads) {
+    const int i = base + tid;
+    const int c = i < n ? count_of(i) : -1;
+    s_c[tid] = c;
+    __syncthreads();
+    int before = 0;
+    bool last = true;
+    for (int t = 0; t < kThreads; ++t) {
+      const int x = s_c[t];
+      before += (t < tid && x == c) ? 1 : 0;
+      last = last && !(t > tid && x == c);
+    }
+    int start = 0;
+    if (i < n) {
+      start = ld(hist + c);
+      order[start + before] = i;
+    }
+    __threadfence();
+    __syncthreads();
+    if (i < n && last) st(hist + c, start + before + 1);
+    __threadfence();
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
 hipError_t launch_map(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,
@@ -226,6 +302,8 @@ hipError_t launch_map(const pba_pack* packs, int n_packs, const int32_t* resp_le
   const int64_t lists = (int64_t)m.B * (m.nqt + m.nkt);
   map_lists<<<(unsigned)((lists + 3) / 4), kThreads, 0, stream>>>(m.cls, m.B, m.nqt, m.nkt, m.status, m.q2k_cnt,
                                                                  m.q2k_idx, m.k2q_cnt, m.k2q_idx);
+  map_order<<<2, kThreads, 0, stream>>>(m.B, m.nqt, m.nkt, m.status, m.q2k_cnt, m.k2q_cnt, m.q_order, m.k_order,
+                                        m.work);
   return hipGetLastError();
 }
 

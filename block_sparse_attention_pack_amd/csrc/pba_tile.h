@@ -36,6 +36,67 @@ __device__ __forceinline__ bf16x8 lds_tr8(const bf16* M, int stride, int r0, int
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Read-only map arrays through the constant address space, so that
+// wave-uniform indices become scalar loads (they then never wait behind the
+// vector-memory counter that also tracks the tile loads).
+typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
+__device__ __forceinline__ cint_ptr cptr(const int32_t* p) { return (cint_ptr)p; }
+
+// Buffer resource over rows [0, S) of a bf16 array with rows of D elements
+// every row_stride elements, starting at `base`.  Offsets past the last
+// row's data read as zero (hardware range check on the per-lane offset).
+// The host guarantees S * row_stride * 2 < 2^31.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16* base, int S, int row_stride, int D) {
+  const int nbytes = ((S - 1) * row_stride + D) * 2;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nbytes, 0x00020000);
+}
+
+// Direct buffer->LDS staging of 64 rows x D into an LDS tile with padded
+// rows of STR elements.  A wave instruction fills 1 KB of LDS in lane order,
+// so lane L of instruction q owns LDS bytes 1024*q + 16*L; the row and chunk
+// there decide which global chunk it fetches (lanes in a row's padding fetch
+// that row's last chunk again; the padding is never read).
+template <int D, int STR>
+struct Stager {
+  static constexpr int NI = 64 * STR * 2 / 1024;  // 1 KB instructions per tile
+  static constexpr int PER_WAVE = (NI + 3) / 4;
+  static_assert((64 * STR * 2) % 1024 == 0, "tile must be whole 1 KB blocks");
+  int off[PER_WAVE];  // byte offset of this lane's chunk relative to row k0
+  int w;
+
+  __device__ __forceinline__ Stager(int tid, int row_stride_bytes) {
+    w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int chunk = 64 * (w * PER_WAVE + i) + lane;
+      const int r = min(chunk / (STR / 8), 63), c = min(chunk % (STR / 8), D / 8 - 1);
+      off[i] = r * row_stride_bytes + 16 * c;
+    }
+  }
+  // Rows k0 .. k0+63 of `rs` into lds_tile (row offset k0 * row_stride_bytes).
+  // (The builtin exists only for the device; the host pass, which never runs
+  // this, must not instantiate it or it drops the kernels' host stubs.)
+  __device__ __forceinline__ void stage(bf16* lds_tile, __amdgpu_buffer_rsrc_t rs, int k0_bytes) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int q = w * PER_WAVE + i;
+      if (q < NI)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (PBA_LDS void*)(lds_tile + 512 * q), 16, off[i] + k0_bytes, 0,
+                                                 0, 0);
+    }
+#endif
+  }
+};
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Keeps the instruction scheduler from moving anything across this point
+// (used between the phases of a tile so that operand loads of a later
+// phase are not hoisted, which would cost registers).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int base) {
   bf16x8 r;
 #pragma unroll

@@ -116,7 +116,12 @@ typedef struct {
  *   k2q_cnt / k2q_idx: the same per key tile over query tiles ([B*nkt*2],
  *       [B*nkt*nqt]).
  *   totals[3] = {n_full, n_partial, n_skip} over all rows.
- *   status[2] = {PBA_DESC_* code, first offending pack or -1}.            */
+ *   status[2] = {PBA_DESC_* code, first offending pack or -1}.
+ *   q_order[B*nqt]: the query tiles b*nqt + qt sorted by visit count
+ *       (n_full + n_partial) descending, ties by index ascending: the
+ *       order in which the query-major kernels take their work, longest
+ *       first.  k_order[B*nkt]: the same for the key tiles.
+ *   work: the map kernels' own scratch (histograms), contents unspecified. */
 typedef struct {
   int32_t B, S, block_m, block_n, nqt, nkt;
   int32_t* tok_pack;
@@ -129,6 +134,9 @@ typedef struct {
   int32_t* k2q_idx;
   int64_t* totals;
   int32_t* status;
+  int32_t* q_order;
+  int32_t* k_order;
+  int32_t* work;
 } pba_block_map;
 
 /* Error message for a return code or device status code (static string). */

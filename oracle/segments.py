@@ -147,6 +147,10 @@ def block_map(packs, resp_len, B, S, BM, BN):
     q2k lists, per (b, qt): the full kt ascending, then the partial kt
     ascending, then -1; counts (n_full, n_partial).  k2q is the same per
     (b, kt) over qt.  totals = (n_full, n_partial, n_skip).
+    q_order: the flat query-tile indices b*nqt + qt sorted by visit count
+    (n_full + n_partial) descending, ties by index ascending; k_order the
+    same over b*nkt + kt.  (A work order, longest lists first; it does not
+    change what is computed.)
     """
     nqt = -(-S // BM)
     nkt = -(-S // BN)
@@ -181,7 +185,13 @@ def block_map(packs, resp_len, B, S, BM, BN):
             part = [qt for qt in range(nqt) if cls[b, qt, kt] == 1]
             k2q_cnt[b, kt] = (len(full), len(part))
             k2q_idx[b, kt, :len(full) + len(part)] = full + part
+    def longest_first(cnt):
+        visits = cnt.reshape(-1, 2).sum(axis=1)
+        keyed = sorted(range(len(visits)), key=lambda i: (-int(visits[i]), i))
+        return np.asarray(keyed, dtype=np.int32)
+
     out.update(
+        q_order=longest_first(q2k_cnt), k_order=longest_first(k2q_cnt),
         tok_win=win, cls=cls, q2k_cnt=q2k_cnt, q2k_idx=q2k_idx, k2q_cnt=k2q_cnt, k2q_idx=k2q_idx,
         totals=np.array([(cls == 2).sum(), (cls == 1).sum(), (cls == 0).sum()], dtype=np.int64),
     )

@@ -51,9 +51,9 @@ def test_host_argument_errors():
     assert A.map_bytes(0, 10, 64, 64) == 0
     assert A.map_bytes(1, 10, 48, 64) == 0
     assert A.workspace_bytes(1, 10, 4, 80) == 0
-    assert A.fwd_tile(32, 8, 128) == (64, 64)
-    assert A.fwd_tile(4, 2, 64) == (128, 64)
-    assert A.fwd_tile(2, 2, 64) == (256, 64)
+    assert A.fwd_tile(32, 8, 128) == (32, 64)
+    assert A.fwd_tile(4, 2, 64) == (64, 64)
+    assert A.fwd_tile(2, 2, 64) == (128, 64)
     assert A.bwd_tile(32, 8, 128) == (64, 128)
     lib = A._lib
     # null map / null pointers are rejected before any device work
@@ -66,7 +66,7 @@ def test_host_argument_errors():
     assert lib.pba_map_init(ctypes.byref(m), 256, 16, 2, 100, 64, 64) == -6
     # map shape mismatches are caught on the host
     assert lib.pba_packed_attn_fwd(ctypes.byref(m), 16, 16, 16, 16, 16, 2, 101, 4, 2, 64, 0.1, None) == -6
-    assert lib.pba_packed_attn_fwd(ctypes.byref(m), 16, 16, 16, 16, 16, 2, 100, 4, 2, 64, 0.1, None) == -5
+    assert lib.pba_packed_attn_fwd(ctypes.byref(m), 16, 16, 16, 16, 16, 2, 100, 4, 4, 64, 0.1, None) == -5
     assert lib.pba_packed_attn_fwd(ctypes.byref(m), 16, 16, 16, 16, 16, 2, 100, 4, 3, 64, 0.1, None) == -3
     assert lib.pba_packed_attn_fwd(ctypes.byref(m), 8, 16, 16, 16, 16, 2, 100, 4, 2, 64, 0.1, None) == -9
     ws = A.workspace_bytes(2, 100, 4, 64)

@@ -10,7 +10,8 @@ from workloads.generate import Pack, PackSet, descriptor_arrays, make_packset, r
 
 pytestmark = pytest.mark.gpu
 
-FIELDS = ("tok_pack", "tok_branch", "tok_win", "cls", "q2k_cnt", "q2k_idx", "k2q_cnt", "k2q_idx", "totals", "status")
+FIELDS = ("tok_pack", "tok_branch", "tok_win", "cls", "q2k_cnt", "q2k_idx", "k2q_cnt", "k2q_idx", "totals", "status",
+          "q_order", "k_order")
 
 
 def _compare(ps, bm, bn):

@@ -24,6 +24,9 @@ def _parse_map_fixture(path):
         while i < len(lines) and not lines[i].startswith("cls"):
             if lines[i] == "k2q":
                 cur = "k2q"
+            elif lines[i].startswith(("qorder:", "korder:")):
+                name, rest = lines[i].split(":")
+                lists[name] = [int(x) for x in rest.split()]
             else:
                 _, rest = lines[i].split(":")
                 full, part = rest.split("|")
@@ -45,8 +48,33 @@ def test_tiny_pack_worked_map(golden_dir):
                 n = len(full) + len(part)
                 assert m[idx][0, t, :n].tolist() == full + part
                 assert (m[idx][0, t, n:] == -1).all()
+        assert m["q_order"].tolist() == lists["qorder"]
+        assert m["k_order"].tolist() == lists["korder"]
     m = oracle.block_map(P, R, 1, 144, 64, 64)
     assert m["totals"].tolist() == [1, 5, 3]
+
+
+def test_work_order_ties_across_rows():
+    """Two identical rows of the tiny pack: visit counts per flat query tile
+    are [1, 2, 3, 1, 2, 3], so longest-first with index tie-breaks gives
+    [2, 5, 1, 4, 0, 3]; key tiles [3, 2, 1, 3, 2, 1] give [0, 3, 1, 4, 2, 5]."""
+    P, R = descriptors([(0, 0, 64, (32, 48)), (1, 0, 64, (32, 48))])
+    m = oracle.block_map(P, R, 2, 144, 64, 64)
+    assert m["q_order"].tolist() == [2, 5, 1, 4, 0, 3]
+    assert m["k_order"].tolist() == [0, 3, 1, 4, 2, 5]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_work_order_is_a_sorted_permutation(seed):
+    rng = np.random.default_rng(300 + seed)
+    ps = random_packset(rng, B=3, S=int(rng.integers(30, 300)), max_packs_per_row=3, max_resp=4, max_len=60)
+    P, R = descriptor_arrays(ps)
+    m = oracle.block_map(P, R, ps.B, ps.S, 32, 16)
+    for order, cnt in ((m["q_order"], m["q2k_cnt"]), (m["k_order"], m["k2q_cnt"])):
+        visits = cnt.reshape(-1, 2).sum(axis=1)
+        assert sorted(order.tolist()) == list(range(len(visits)))
+        for a, b in zip(order[:-1], order[1:]):
+            assert visits[a] > visits[b] or (visits[a] == visits[b] and a < b)
 
 
 def _brute_cls(mask_b, S, BM, BN):
