@@ -1,10 +1,10 @@
 #!/usr/bin/env python3
 """Throughput of packed branch-aware attention (fwd + bwd) on one MI355X.
 
-One step = the whole hot path over one batch: build the forward and backward
-block maps from the pack descriptors, the forward kernel, then the three
-backward stages (rowsum(dO*O) pass, main kernel, dQ convert).  Inputs are
-resident in HBM before timing; outputs, maps and workspace are preallocated.
+One step = the whole hot path over one batch: build the query-major and
+key-major block maps from the pack descriptors, the forward kernel, then the
+two backward kernels (dQ with rowsum(dO*O), then dK/dV).  Inputs are resident
+in HBM before timing; outputs, maps and workspace are preallocated.
 
 Metric: useful TFLOP/s = 14 * D * Hq * (allowed query-key pairs) per step /
 step time (4*D forward + 10*D backward per allowed pair and q head; masked
@@ -83,7 +83,7 @@ class Runner:
         self.A.packed_attn_fwd(self.fmap, self.q, self.k, self.v, self.scale, out=(self.o, self.lse))
 
     def bwd(self, stages):
-        self.A.packed_attn_bwd(self.bmap, self.q, self.k, self.v, self.o, self.lse, self.do, self.scale,
+        self.A.packed_attn_bwd(self.fmap, self.bmap, self.q, self.k, self.v, self.o, self.lse, self.do, self.scale,
                                out=(self.dq, self.dk, self.dv), workspace=self.ws, stages=stages)
 
     def step(self, ev=None):
@@ -95,28 +95,26 @@ class Runner:
         rec(1)
         self.fwd()
         rec(2)
-        self.bwd(A.BWD_PREPROCESS)
+        self.bwd(A.BWD_DQ)
         rec(3)
-        self.bwd(A.BWD_MAIN)
+        self.bwd(A.BWD_DKDV)
         rec(4)
-        self.bwd(A.BWD_FINALIZE)
-        rec(5)
 
 
 def time_runner(torch, r, steps, warmup):
     for _ in range(warmup):
         r.step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         r.step(evs[i])
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    names = ["map", "fwd", "bwd_pre", "bwd_main", "bwd_fin"]
+    names = ["map", "fwd", "bwd_dq", "bwd_dkdv"]
     per = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps for i, n in enumerate(names)}
-    per["step_events"] = sum(e[0].elapsed_time(e[5]) for e in evs) / steps
+    per["step_events"] = sum(e[0].elapsed_time(e[4]) for e in evs) / steps
     return wall * 1e3, per
 
 
@@ -131,7 +129,7 @@ def allowed_pairs(ps):
 
 def map_bytes(r, m):
     B, S = r.ps.B, r.ps.S
-    return (20 * r.n_packs + 4 * r.n_resp + 24 * B * S + 9 * B * m.nqt * m.nkt + 8 * B * (m.nqt + m.nkt))
+    return (20 * r.n_packs + 4 * r.n_resp + 24 * B * S + 9 * B * m.nqt * m.nkt + 12 * B * (m.nqt + m.nkt))
 
 
 def traffic_record(kernel):
@@ -240,17 +238,17 @@ def main():
     value = useful / (ms * 1e-3) / 1e12
     log(f"step {ms:.3f} ms  useful {value:.1f} TFLOP/s  per-kernel ms {json.dumps({k_: round(v_, 4) for k_, v_ in per.items()})}")
 
-    fwd_flops, bwd_flops = 4.0 * w.D * w.Hq * n_allowed, 10.0 * w.D * w.Hq * n_allowed
-    kern = {
-        "fwd": {"ms": per["fwd"], "useful_tflops": fwd_flops / (per["fwd"] * 1e-3) / 1e12},
-        "bwd_main": {"ms": per["bwd_main"], "useful_tflops": bwd_flops / (per["bwd_main"] * 1e-3) / 1e12},
-        "map": {"ms": per["map"], "GBps": (map_bytes(r, r.fmap) + map_bytes(r, r.bmap)) / (per["map"] * 1e-3) / 1e9},
-        "bwd_pre": {"ms": per["bwd_pre"],
-                    "GBps": ps.B * ps.S * w.Hq * (8.0 * w.D + 4) / (per["bwd_pre"] * 1e-3) / 1e9},
-        "bwd_fin": {"ms": per["bwd_fin"], "GBps": ps.B * ps.S * w.Hq * 6.0 * w.D / (per["bwd_fin"] * 1e-3) / 1e9},
-    }
-    dom = "bwd_main" if per["bwd_main"] >= per["fwd"] else "fwd"
-    achieved = kern[dom]["useful_tflops"]
+    # Useful FLOPs per allowed (query, key) pair and q head: 4*D forward,
+    # 10*D backward.  Per kernel, its own MFMA work on allowed pairs: the dQ
+    # kernel recomputes Q K^T and forms dO V^T and dS K (6*D), the dK/dV
+    # kernel recomputes Q K^T and dO V^T and forms P^T dO and dS^T Q (8*D).
+    per_pair = {"fwd": 4.0, "bwd_dq": 6.0, "bwd_dkdv": 8.0}
+    kern = {name: {"ms": per[name], "tflops_on_allowed_pairs": f * w.D * w.Hq * n_allowed / (per[name] * 1e-3) / 1e12,
+                   "flop_per_allowed_pair_per_head": f * w.D}
+            for name, f in per_pair.items()}
+    kern["map"] = {"ms": per["map"], "GBps": (map_bytes(r, r.fmap) + map_bytes(r, r.bmap)) / (per["map"] * 1e-3) / 1e9}
+    dom = max(per_pair, key=lambda k_: per[k_])
+    achieved = kern[dom]["tflops_on_allowed_pairs"]
     tr = traffic_record(dom)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS,
@@ -266,7 +264,7 @@ def main():
     if not args.no_baselines:
         rd = Runner(A, torch, ps, q, k, v, do, w.Hq, w.Hkv, w.D, w.scale, dense=True)
         ms_d, per_d = time_runner(torch, rd, args.steps, args.warmup)
-        att = lambda p: p["fwd"] + p["bwd_pre"] + p["bwd_main"] + p["bwd_fin"]  # noqa: E731
+        att = lambda p: p["fwd"] + p["bwd_dq"] + p["bwd_dkdv"]  # noqa: E731
         del rd
         pps, pairs = pairwise_packset(ps)
         pt = [pairwise_tensors(x, pairs, pps.S).to(dev).contiguous() for x in (w.q, w.k, w.v, w.do)]

@@ -59,12 +59,12 @@ _lib.pba_packed_attn_fwd.argtypes = [ctypes.POINTER(PbaBlockMap)] + [ctypes.c_vo
 _lib.pba_packed_attn_fwd.restype = ctypes.c_int
 _lib.pba_bwd_workspace_bytes.argtypes = [ctypes.c_int] * 4
 _lib.pba_bwd_workspace_bytes.restype = ctypes.c_size_t
-_lib.pba_packed_attn_bwd.argtypes = [ctypes.POINTER(PbaBlockMap)] + [ctypes.c_void_p] * 10 + [ctypes.c_size_t] + \
+_lib.pba_packed_attn_bwd.argtypes = [ctypes.POINTER(PbaBlockMap)] * 2 + [ctypes.c_void_p] * 10 + [ctypes.c_size_t] + \
     [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_void_p]
 _lib.pba_packed_attn_bwd.restype = ctypes.c_int
 _lib.pba_packed_attn_bwd_stages.argtypes = [ctypes.c_int] + list(_lib.pba_packed_attn_bwd.argtypes)
 _lib.pba_packed_attn_bwd_stages.restype = ctypes.c_int
-BWD_PREPROCESS, BWD_MAIN, BWD_FINALIZE, BWD_ALL = 1, 2, 4, 7
+BWD_DQ, BWD_DKDV, BWD_ALL = 1, 2, 3
 
 
 class PbaError(RuntimeError):
@@ -225,11 +225,12 @@ def packed_attn_fwd(m: BlockMap, q, k, v, softmax_scale: Optional[float] = None,
     return o, lse
 
 
-def packed_attn_bwd(m: BlockMap, q, k, v, o, lse, dout, softmax_scale: Optional[float] = None,
+def packed_attn_bwd(qmap: BlockMap, kmap: BlockMap, q, k, v, o, lse, dout, softmax_scale: Optional[float] = None,
                     out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
-                    workspace: Optional[torch.Tensor] = None, stream=None, stages: int = 7):
-    """dQ, dK, dV (bf16) for the loss <dO, O>.  `stages` selects a subset of
-    the backward's stages (BWD_PREPROCESS | BWD_MAIN | BWD_FINALIZE)."""
+                    workspace: Optional[torch.Tensor] = None, stream=None, stages: int = BWD_ALL):
+    """dQ, dK, dV (bf16) for the loss <dO, O>.  qmap has the forward's tile
+    shape (fwd_tile), kmap the backward's (bwd_tile).  `stages` selects a
+    subset of the backward's stages (BWD_DQ | BWD_DKDV)."""
     for n, x in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         _bf16(x, n)
     B, S, Hq, D = q.shape
@@ -244,8 +245,9 @@ def packed_attn_bwd(m: BlockMap, q, k, v, o, lse, dout, softmax_scale: Optional[
         workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
     base = workspace.data_ptr()
     off = (-base) % 256
-    _check(_lib.pba_packed_attn_bwd_stages(stages, ctypes.byref(m.struct), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                    lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                                    base + off, workspace.numel() - off, B, S, Hq, Hkv, D, scale, _stream(stream)),
+    _check(_lib.pba_packed_attn_bwd_stages(stages, ctypes.byref(qmap.struct), ctypes.byref(kmap.struct), q.data_ptr(),
+                                           k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), base + off,
+                                           workspace.numel() - off, B, S, Hq, Hkv, D, scale, _stream(stream)),
            "pba_packed_attn_bwd_stages")
     return dq, dk, dv

@@ -8,10 +8,6 @@
 
 #include "pba_internal.h"
 
-namespace pba {
-int fwd_wg_heads(int G);
-}
-
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -96,6 +92,18 @@ int check_heads(int B, int S, int Hq, int Hkv, int D) {
   return PBA_OK;
 }
 
+// The softmax is evaluated as exp2(s * scale * log2(e) - m) with the row
+// maximum taken before scaling, which needs a positive, finite scale.
+int check_scale(float scale) {
+  return (scale > 0.f && scale < 3.0e38f) ? PBA_OK : PBA_ERR_SCALE;
+}
+
+// Tiles are read through buffer resources with 32-bit byte offsets: one
+// batch row of the widest tensor ([S, Hq, D] bf16) must stay below 2 GiB.
+int check_row_bytes(int S, int Hq, int D) {
+  return (int64_t)S * Hq * D * 2 < ((int64_t)1 << 31) ? PBA_OK : PBA_ERR_SHAPE;
+}
+
 pba::MapView view_of(const pba_block_map* m) {
   pba::MapView v;
   v.B = m->B; v.S = m->S; v.bm = m->block_m; v.bn = m->block_n; v.nqt = m->nqt; v.nkt = m->nkt;
@@ -121,6 +129,7 @@ const char* pba_strerror(int code) {
     case PBA_ERR_WORKSPACE: return "backward workspace missing or too small";
     case PBA_ERR_DEVICE: return "no gfx950 device current, or a HIP launch failed";
     case PBA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case PBA_ERR_SCALE: return "softmax scale must be positive and finite";
     case PBA_DESC_ROW: return "descriptor: row outside [0, B)";
     case PBA_DESC_NEGATIVE: return "descriptor: negative start, length or response count";
     case PBA_DESC_RESP_RANGE: return "descriptor: response range outside resp_len";
@@ -205,6 +214,8 @@ int pba_packed_attn_fwd(const pba_block_map* map, const void* q, const void* k, 
                         int B, int S, int Hq, int Hkv, int D, float softmax_scale, void* stream) {
   if (!q || !k || !v || !o || !lse) return PBA_ERR_NULL;
   if (int rc = check_heads(B, S, Hq, Hkv, D)) return rc;
+  if (int rc = check_scale(softmax_scale)) return rc;
+  if (int rc = check_row_bytes(S, Hq, D)) return rc;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return PBA_ERR_ALIGN;
   int bm, bn;
   pba_fwd_tile(Hq, Hkv, D, &bm, &bn);
@@ -229,28 +240,33 @@ int pba_packed_attn_fwd(const pba_block_map* map, const void* q, const void* k, 
 
 size_t pba_bwd_workspace_bytes(int B, int S, int Hq, int D) {
   if (B < 1 || B > kMaxB || S < 1 || S > kMaxS || Hq < 1 || Hq > kMaxHeads || (D != 64 && D != 128)) return 0;
-  return align_up((size_t)B * S * Hq * D * 4) + align_up((size_t)B * Hq * S * 4);
+  return 2 * align_up((size_t)B * Hq * S * 4);
 }
 
-int pba_packed_attn_bwd_stages(int stages, const pba_block_map* map, const void* q, const void* k, const void* v,
-                               const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                               void* workspace, size_t workspace_bytes, int B, int S, int Hq, int Hkv, int D,
-                               float softmax_scale, void* stream) {
+int pba_packed_attn_bwd_stages(int stages, const pba_block_map* qmap, const pba_block_map* kmap, const void* q,
+                               const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int S,
+                               int Hq, int Hkv, int D, float softmax_scale, void* stream) {
   if (stages < 1 || stages > PBA_BWD_ALL) return PBA_ERR_SHAPE;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return PBA_ERR_NULL;
   if (int rc = check_heads(B, S, Hq, Hkv, D)) return rc;
+  if (int rc = check_scale(softmax_scale)) return rc;
+  if (int rc = check_row_bytes(S, Hq, D)) return rc;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
       !aligned16(dk) || !aligned16(dv))
     return PBA_ERR_ALIGN;
   int bm, bn;
+  pba_fwd_tile(Hq, Hkv, D, &bm, &bn);
+  if (int rc = check_map(qmap, B, S, bm, bn)) return rc;
   pba_bwd_tile(Hq, Hkv, D, &bm, &bn);
-  if (int rc = check_map(map, B, S, bm, bn)) return rc;
+  if (int rc = check_map(kmap, B, S, bm, bn)) return rc;
   const size_t need = pba_bwd_workspace_bytes(B, S, Hq, D);
   if (!workspace || workspace_bytes < need) return PBA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return PBA_ERR_ALIGN;
   if (int rc = device_ok()) return rc;
   pba::BwdArgs a;
-  a.map = view_of(map);
+  a.qmap = view_of(qmap);
+  a.kmap = view_of(kmap);
   a.q = static_cast<const pba::bf16*>(q);
   a.k = static_cast<const pba::bf16*>(k);
   a.v = static_cast<const pba::bf16*>(v);
@@ -260,8 +276,8 @@ int pba_packed_attn_bwd_stages(int stages, const pba_block_map* map, const void*
   a.dq = static_cast<pba::bf16*>(dq);
   a.dk = static_cast<pba::bf16*>(dk);
   a.dv = static_cast<pba::bf16*>(dv);
-  a.dq_acc = static_cast<float*>(workspace);
-  a.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up((size_t)B * S * Hq * D * 4));
+  a.delta = static_cast<float*>(workspace);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up((size_t)B * Hq * S * 4));
   a.B = B;
   a.S = S;
   a.Hq = Hq;
@@ -273,12 +289,12 @@ int pba_packed_attn_bwd_stages(int stages, const pba_block_map* map, const void*
   return e == hipSuccess ? PBA_OK : PBA_ERR_DEVICE;
 }
 
-int pba_packed_attn_bwd(const pba_block_map* map, const void* q, const void* k, const void* v, const void* o,
-                        const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
-                        size_t workspace_bytes, int B, int S, int Hq, int Hkv, int D, float softmax_scale,
-                        void* stream) {
-  return pba_packed_attn_bwd_stages(PBA_BWD_ALL, map, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
-                                    B, S, Hq, Hkv, D, softmax_scale, stream);
+int pba_packed_attn_bwd(const pba_block_map* qmap, const pba_block_map* kmap, const void* q, const void* k,
+                        const void* v, const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, int B, int S, int Hq, int Hkv, int D,
+                        float softmax_scale, void* stream) {
+  return pba_packed_attn_bwd_stages(PBA_BWD_ALL, qmap, kmap, q, k, v, o, lse, dout, dq, dk, dv, workspace,
+                                    workspace_bytes, B, S, Hq, Hkv, D, softmax_scale, stream);
 }
 
 }  // extern "C"

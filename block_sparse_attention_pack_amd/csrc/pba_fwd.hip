@@ -151,10 +151,10 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   const cint_ptr list = cptr(mp.q2k_idx) + lrow * mp.nkt;
 
   const int kvstride = Hkv * D;
-  const __amdgpu_buffer_rsrc_t krs = rows_rsrc(a.k + ((int64_t)b * S * Hkv + g) * D, S, kvstride, D);
-  const __amdgpu_buffer_rsrc_t vrs = rows_rsrc(a.v + ((int64_t)b * S * Hkv + g) * D, S, kvstride, D);
-  const Stager<D, C::KSTR> kst(tid, kvstride * 2);
-  const Stager<D, C::VSTR> vst(tid, kvstride * 2);
+  const bf16* kb = a.k + ((int64_t)b * S * Hkv + g) * D;
+  const bf16* vb = a.v + ((int64_t)b * S * Hkv + g) * D;
+  const Stager<D, C::KSTR> kst(tid, kvstride);
+  const Stager<D, C::VSTR> vst(tid, kvstride);
 
   float m = kNegInf, l = 0.f;
   f32x16 o[C::NE];
@@ -162,9 +162,9 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   for (int e = 0; e < C::NE; ++e) o[e] = f32x16{};
 
   if (n > 0) {
-    const int k0b = min(max(list[0], 0), mp.nkt - 1) * 64 * kvstride * 2;
-    kst.stage(sK[0], krs, k0b);
-    vst.stage(sV[0], vrs, k0b);
+    const int k0 = min(max(list[0], 0), mp.nkt - 1) * 64;
+    kst.stage(sK[0], kb + (int64_t)k0 * kvstride, S - k0);
+    vst.stage(sV[0], vb + (int64_t)k0 * kvstride, S - k0);
   }
   wait_vmem();
   __syncthreads();
@@ -173,9 +173,9 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
     const int buf = j & 1;
     // The other buffer was last read in step j-1, which every wave has left.
     if (j + 1 < n) {
-      const int k0b = min(max(list[j + 1], 0), mp.nkt - 1) * 64 * kvstride * 2;
-      kst.stage(sK[buf ^ 1], krs, k0b);
-      vst.stage(sV[buf ^ 1], vrs, k0b);
+      const int k0 = min(max(list[j + 1], 0), mp.nkt - 1) * 64;
+      kst.stage(sK[buf ^ 1], kb + (int64_t)k0 * kvstride, S - k0);
+      vst.stage(sV[buf ^ 1], vb + (int64_t)k0 * kvstride, S - k0);
     }
     if (j < nfull) {
       fwd_tile<D, false>(o, m, l, qop, sK[buf], sV[buf], a.scale_log2, 0, 0, 0, 0, lane);

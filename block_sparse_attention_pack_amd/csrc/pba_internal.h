@@ -21,8 +21,8 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 // Tile shapes of the attention kernels (query tokens x key tokens).
 constexpr int kFwdBM = 32;   // one wave owns 32 query rows of one q head
 constexpr int kFwdBN = 64;
-constexpr int kBwdBM = 64;   // query rows per backward step
-constexpr int kBwdBN = 128;  // key rows per backward workgroup (4 waves x 32)
+constexpr int kBwdBM = 64;   // query rows per dK / dV step
+constexpr int kBwdBN = 128;  // key rows per dK / dV workgroup (4 waves x 32)
 
 struct MapView {  // device-side view of a pba_block_map
   int B, S, bm, bn, nqt, nkt;
@@ -48,7 +48,8 @@ struct FwdArgs {
 };
 
 struct BwdArgs {
-  MapView map;
+  MapView qmap;  // query-major map, forward tile shape (bwd_dq)
+  MapView kmap;  // key-major map, backward tile shape (bwd_dkdv)
   const bf16* q;
   const bf16* k;
   const bf16* v;
@@ -58,8 +59,8 @@ struct BwdArgs {
   bf16* dq;
   bf16* dk;
   bf16* dv;
-  float* dq_acc;  // [B, S, Hq, D] fp32
-  float* delta;   // [B, Hq, S]  fp32 rowsum(dO * O)
+  float* delta;  // [B, Hq, S] fp32 rowsum(dO * O), written by bwd_dq
+  float* lse2;   // [B, Hq, S] fp32 LSE * log2(e) (0 for rows that see nothing)
   int B, S, Hq, Hkv, G;
   float scale, scale_log2;
 };
@@ -70,8 +71,10 @@ constexpr float kLog2eHost = 1.4426950408889634f;
 hipError_t launch_map(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,
                       const pba_block_map& map, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int D, int B, hipStream_t stream);
-// Backward stages (bit mask): delta + accumulator clear, main, dQ convert.
-constexpr int kBwdPre = 1, kBwdMain = 2, kBwdFin = 4, kBwdAll = 7;
+// Backward stages (bit mask): dQ (and Delta, LSE2), then dK / dV.
+constexpr int kBwdDq = 1, kBwdDkdv = 2, kBwdAll = 3;
 hipError_t launch_bwd(const BwdArgs& a, int D, int stages, hipStream_t stream);
+// q heads per forward / dQ workgroup for G q heads per kv head.
+int fwd_wg_heads(int G);
 
 }  // namespace pba

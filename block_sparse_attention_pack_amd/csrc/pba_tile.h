@@ -36,18 +36,25 @@ __device__ __forceinline__ bf16x8 lds_tr8(const bf16* M, int stride, int r0, int
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Makes v opaque to the optimiser so that it stays in its own register for
+// as long as it lives.  Used for the per-lane offsets of LDS-DMA loads: the
+// compiler treats such a load as a store, so overwriting its offset register
+// while it is in flight costs a wait for all outstanding loads, and a
+// rematerialised (recomputed) offset would be overwritten right away.
+__device__ __forceinline__ void pin(int& v) { asm volatile("" : "+v"(v)); }
+
 // Read-only map arrays through the constant address space, so that
 // wave-uniform indices become scalar loads (they then never wait behind the
 // vector-memory counter that also tracks the tile loads).
 typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
 __device__ __forceinline__ cint_ptr cptr(const int32_t* p) { return (cint_ptr)p; }
 
-// Buffer resource over rows [0, S) of a bf16 array with rows of D elements
+// Buffer resource over `rows` rows of a bf16 array with rows of D elements
 // every row_stride elements, starting at `base`.  Offsets past the last
 // row's data read as zero (hardware range check on the per-lane offset).
-// The host guarantees S * row_stride * 2 < 2^31.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16* base, int S, int row_stride, int D) {
-  const int nbytes = ((S - 1) * row_stride + D) * 2;
+// The host guarantees that a batch row of every tensor is under 2 GiB.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16* base, int rows, int row_stride, int D) {
+  const int nbytes = ((rows - 1) * row_stride + D) * 2;
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nbytes, 0x00020000);
 }
 
@@ -55,40 +62,89 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16* base, in
 // rows of STR elements.  A wave instruction fills 1 KB of LDS in lane order,
 // so lane L of instruction q owns LDS bytes 1024*q + 16*L; the row and chunk
 // there decide which global chunk it fetches (lanes in a row's padding fetch
-// that row's last chunk again; the padding is never read).
+// that row's last chunk again; the padding is never read).  The per-lane
+// offsets are fixed for the whole kernel; the tile's position goes into the
+// (scalar) buffer resource, whose range ends at the last valid row, so rows
+// past the end of the sequence read as zeros.
 template <int D, int STR>
 struct Stager {
   static constexpr int NI = 64 * STR * 2 / 1024;  // 1 KB instructions per tile
   static constexpr int PER_WAVE = (NI + 3) / 4;
   static_assert((64 * STR * 2) % 1024 == 0, "tile must be whole 1 KB blocks");
-  int off[PER_WAVE];  // byte offset of this lane's chunk relative to row k0
+  int off[PER_WAVE];  // byte offset of this lane's chunk from the tile's first row
   int w;
+  int row_stride;
 
-  __device__ __forceinline__ Stager(int tid, int row_stride_bytes) {
+  __device__ __forceinline__ Stager(int tid, int row_stride_elems) : row_stride(row_stride_elems) {
     w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int chunk = 64 * (w * PER_WAVE + i) + lane;
       const int r = min(chunk / (STR / 8), 63), c = min(chunk % (STR / 8), D / 8 - 1);
-      off[i] = r * row_stride_bytes + 16 * c;
+      off[i] = r * row_stride_elems * 2 + 16 * c;
+      pin(off[i]);
     }
   }
-  // Rows k0 .. k0+63 of `rs` into lds_tile (row offset k0 * row_stride_bytes).
+  // Rows [0, 64) of the tile starting at `tile`, of which `rows` (>= 1) are
+  // valid, into lds_tile.
   // (The builtin exists only for the device; the host pass, which never runs
   // this, must not instantiate it or it drops the kernels' host stubs.)
-  __device__ __forceinline__ void stage(bf16* lds_tile, __amdgpu_buffer_rsrc_t rs, int k0_bytes) const {
+  __device__ __forceinline__ void stage(bf16* lds_tile, const bf16* tile, int rows) const {
 #if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rs = rows_rsrc(tile, rows, row_stride, D);
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int q = w * PER_WAVE + i;
-      if (q < NI)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (PBA_LDS void*)(lds_tile + 512 * q), 16, off[i] + k0_bytes, 0,
-                                                 0, 0);
+      if (q < NI) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (PBA_LDS void*)(lds_tile + 512 * q), 16, off[i], 0, 0, 0);
     }
 #endif
   }
 };
+
+// Register staging of 64 rows x D (256 threads): thread tid holds the
+// 16-byte chunks tid + 256*i, i < CH, of the tile in row-major chunk order.
+// Loads go through a buffer resource whose range ends at the last valid row
+// (rows past it read as zero); the per-lane offsets are fixed, the tile's
+// position is in the (scalar) resource.
+template <int D, int STR>
+struct RegStager {
+  static constexpr int CH = 64 * D / 8 / 256;
+  int off[CH];  // byte offset of chunk i from the tile's first row
+  int row_stride;
+
+  __device__ __forceinline__ RegStager(int tid, int row_stride_elems) : row_stride(row_stride_elems) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + 256 * i;
+      off[i] = (c / (D / 8)) * row_stride_elems * 2 + 16 * (c % (D / 8));
+    }
+  }
+  __device__ __forceinline__ void load(u32x4 (&r)[CH], const bf16* tile, int rows) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rs = rows_rsrc(tile, rows, row_stride, D);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], 0, 0));
+#endif
+  }
+  __device__ __forceinline__ static void store(bf16* lds_tile, const u32x4 (&r)[CH], int tid) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + 256 * i;
+      *(u32x4*)(lds_tile + (c / (D / 8)) * STR + 8 * (c % (D / 8))) = r[i];
+    }
+  }
+};
+
+// src[0..63] (fp32, of which the first n >= 1 are valid; the rest read as
+// 0) straight into LDS dst[0..63], one value per lane; lane4 = 4 * lane,
+// pinned by the caller.
+__device__ __forceinline__ void buffer_lds_dword(const float* src, int n, float* dst, int lane4) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, n * 4, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (PBA_LDS void*)dst, 4, lane4, 0, 0, 0);
+#endif
+}
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 

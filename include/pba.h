@@ -69,6 +69,7 @@ extern "C" {
 #define PBA_ERR_WORKSPACE  -7  /* backward workspace missing or too small           */
 #define PBA_ERR_DEVICE     -8  /* no gfx950 device current, or a HIP launch failed  */
 #define PBA_ERR_ALIGN      -9  /* a tensor pointer is not 16-byte aligned          */
+#define PBA_ERR_SCALE     -10  /* softmax_scale not positive and finite            */
 
 /* ---- device status codes (map->status[0]; status[1] = first bad pack) -- */
 #define PBA_DESC_OK          0
@@ -170,44 +171,47 @@ PBA_API int pba_pack_block_map(const pba_pack* packs, int n_packs, const int32_t
  * the backward).  q, k, v, o: bf16 device arrays in the layouts above;
  * lse: fp32 [B, Hq, S].  Only the map's full and partial tiles are
  * computed; the mask is applied on partial tiles only.  The map must have
- * been built for (B, S) with the tile shape of pba_fwd_tile. */
+ * been built for (B, S) with the tile shape of pba_fwd_tile.  softmax_scale
+ * must be positive and finite (PBA_ERR_SCALE).  One batch row of Q must be
+ * under 2 GiB (S * Hq * D * 2 < 2^31, else PBA_ERR_SHAPE). */
 PBA_API int pba_packed_attn_fwd(const pba_block_map* map, const void* q, const void* k, const void* v,
                         void* o, float* lse, int B, int S, int Hq, int Hkv, int D,
                         float softmax_scale, void* stream);
 
-/* Workspace bytes the backward needs (fp32 dQ accumulator and the per-row
- * dot products rowsum(dO * O)); 0 on bad arguments. */
+/* Workspace bytes the backward needs: two fp32 [B, Hq, S] arrays (the row
+ * dot products rowsum(dO * O) and the log2-domain LSE), written by the dQ
+ * stage and read by the dK / dV stage; 0 on bad arguments. */
 PBA_API size_t pba_bwd_workspace_bytes(int B, int S, int Hq, int D);
 
 /* Backward of the forward above for the loss <dO, O>: dQ, dK, dV (bf16),
- * with dK / dV summed over the q heads that share a kv head.  o and lse
- * are the forward's outputs; dout is dO.  workspace: device memory of at
- * least pba_bwd_workspace_bytes bytes, 256-byte aligned, contents
- * irrelevant (overwritten).  The map must have been built for (B, S) with
- * the tile shape of pba_bwd_tile. */
-PBA_API int pba_packed_attn_bwd(const pba_block_map* map, const void* q, const void* k, const void* v,
-                        const void* o, const float* lse, const void* dout,
-                        void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                        int B, int S, int Hq, int Hkv, int D, float softmax_scale, void* stream);
+ * with dK / dV summed over the q heads that share a kv head.  o and lse are
+ * the forward's outputs; dout is dO.  Two maps of the same descriptors:
+ * qmap with the tile shape of pba_fwd_tile (the dQ stage walks query tiles)
+ * and kmap with the tile shape of pba_bwd_tile (the dK / dV stage walks key
+ * tiles).  workspace: device memory of at least pba_bwd_workspace_bytes,
+ * 256-byte aligned, contents irrelevant (overwritten).  Every output
+ * element is written exactly once (no accumulation into the outputs, no
+ * atomics), so the result is deterministic.  softmax_scale > 0. */
+PBA_API int pba_packed_attn_bwd(const pba_block_map* qmap, const pba_block_map* kmap, const void* q, const void* k,
+                                const void* v, const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                                void* dv, void* workspace, size_t workspace_bytes, int B, int S, int Hq, int Hkv,
+                                int D, float softmax_scale, void* stream);
 
-/* The backward in its three stages, for callers that schedule or time them
- * separately.  `stages` is a bit mask; running all three in order on one
- * stream is exactly pba_packed_attn_bwd:
- *   PBA_BWD_PREPROCESS  workspace <- rowsum(dO * O) per (row, q head, token),
- *                       and the fp32 dQ accumulator <- 0
- *   PBA_BWD_MAIN        dK, dV written; scale * dS K added into the dQ
- *                       accumulator (needs the preprocess stage's workspace)
- *   PBA_BWD_FINALIZE    dQ <- bf16(dQ accumulator)
+/* The backward in its two stages, for callers that schedule or time them
+ * separately.  `stages` is a bit mask; running both in order on one stream
+ * is exactly pba_packed_attn_bwd:
+ *   PBA_BWD_DQ    dQ written; workspace <- rowsum(dO * O) and LSE * log2(e)
+ *   PBA_BWD_DKDV  dK, dV written (reads the workspace the dQ stage wrote)
  * Arguments as for pba_packed_attn_bwd (all are checked for every stage);
  * returns PBA_ERR_SHAPE for an empty or unknown mask. */
-#define PBA_BWD_PREPROCESS 1
-#define PBA_BWD_MAIN       2
-#define PBA_BWD_FINALIZE   4
-#define PBA_BWD_ALL        7
-PBA_API int pba_packed_attn_bwd_stages(int stages, const pba_block_map* map, const void* q, const void* k,
-                                       const void* v, const void* o, const float* lse, const void* dout,
-                                       void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                                       int B, int S, int Hq, int Hkv, int D, float softmax_scale, void* stream);
+#define PBA_BWD_DQ   1
+#define PBA_BWD_DKDV 2
+#define PBA_BWD_ALL  3
+PBA_API int pba_packed_attn_bwd_stages(int stages, const pba_block_map* qmap, const pba_block_map* kmap,
+                                       const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                       const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                                       size_t workspace_bytes, int B, int S, int Hq, int Hkv, int D,
+                                       float softmax_scale, void* stream);
 
 #ifdef __cplusplus
 }

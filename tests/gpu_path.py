@@ -36,7 +36,7 @@ def run_fwd_bwd(w, bwd=True):
     out = {"o": o, "lse": lse, "fmap": fm}
     if bwd:
         bm = build_map(w.packset, *A.bwd_tile(w.Hq, w.Hkv, w.D))
-        dq, dk, dv = A.packed_attn_bwd(bm, q, k, v, o, lse, do, w.scale)
+        dq, dk, dv = A.packed_attn_bwd(fm, bm, q, k, v, o, lse, do, w.scale)
         out.update(dq=dq, dk=dk, dv=dv, bmap=bm)
     torch.cuda.synchronize()
     st = fm.status().cpu().tolist()

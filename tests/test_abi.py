@@ -70,9 +70,18 @@ def test_host_argument_errors():
     assert lib.pba_packed_attn_fwd(ctypes.byref(m), 16, 16, 16, 16, 16, 2, 100, 4, 3, 64, 0.1, None) == -3
     assert lib.pba_packed_attn_fwd(ctypes.byref(m), 8, 16, 16, 16, 16, 2, 100, 4, 2, 64, 0.1, None) == -9
     ws = A.workspace_bytes(2, 100, 4, 64)
-    assert ws >= 2 * 100 * 4 * 64 * 4 + 2 * 4 * 100 * 4
+    assert ws >= 2 * 2 * 4 * 100 * 4
     mb = A.PbaBlockMap()
     assert lib.pba_map_init(ctypes.byref(mb), 256, 1 << 20, 2, 100, 64, 128) == 0
-    args = [ctypes.byref(mb)] + [16] * 10
-    assert lib.pba_packed_attn_bwd(*args[:10], 256, 0, 2, 100, 4, 2, 64, 0.1, None) == -7
-    assert lib.pba_packed_attn_bwd(*args[:10], 256, ws - 1, 2, 100, 4, 2, 64, 0.1, None) == -7
+    # (4, 2, 64): forward / dQ tiles 64x64 (map m), dK / dV tiles 64x128 (map mb)
+    args = [ctypes.byref(m), ctypes.byref(mb)] + [16] * 9
+    assert lib.pba_packed_attn_bwd(*args, 256, 0, 2, 100, 4, 2, 64, 0.1, None) == -7
+    assert lib.pba_packed_attn_bwd(*args, 256, ws - 1, 2, 100, 4, 2, 64, 0.1, None) == -7
+    swapped = [ctypes.byref(mb), ctypes.byref(m)] + [16] * 9
+    assert lib.pba_packed_attn_bwd(*swapped, 256, ws, 2, 100, 4, 2, 64, 0.1, None) == -5
+    # the softmax scale must be positive and finite
+    assert lib.pba_packed_attn_fwd(ctypes.byref(m), 16, 16, 16, 16, 16, 2, 100, 4, 2, 64, 0.0, None) == -10
+    assert lib.pba_packed_attn_fwd(ctypes.byref(m), 16, 16, 16, 16, 16, 2, 100, 4, 2, 64, -0.1, None) == -10
+    assert lib.pba_packed_attn_bwd(*args, 256, ws, 2, 100, 4, 2, 64, float("inf"), None) == -10
+    # one batch row of Q must stay under 2 GiB (32-bit buffer offsets)
+    assert lib.pba_packed_attn_fwd(ctypes.byref(m), 16, 16, 16, 16, 16, 2, 1 << 20, 16, 8, 128, 0.1, None) == -2
