@@ -132,16 +132,22 @@ def map_bytes(r, m):
     return (20 * r.n_packs + 4 * r.n_resp + 24 * B * S + 9 * B * m.nqt * m.nkt + 12 * B * (m.nqt + m.nkt))
 
 
+def sources_sha256(names):
+    """sha256 over the named csrc files, in order (identifies a kernel build)."""
+    h = hashlib.sha256()
+    for n in names:
+        h.update(open(os.path.join(ROOT, "block_sparse_attention_pack_amd", "csrc", n), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_record(kernel):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+    taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, "block_sparse_attention_pack_amd", "csrc", rec["source"])
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if sha != rec.get("source_sha256"):
+    if sources_sha256(rec["sources"]) != rec.get("sources_sha256"):
         return None
     return rec
 
@@ -208,6 +214,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baselines", action="store_true", help="skip the dense-map and pairwise-layout runs")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -278,6 +286,15 @@ def main():
             "pairwise_layout": {"B": pps.B, "S": pps.S, "allowed_pairs": allowed_pairs(pps)},
         })
         log(f"dense-map attn {att(per_d):.3f} ms, pairwise attn {att(per_p):.3f} ms, sparse attn {att(per):.3f} ms")
+
+    if args.copy_calibration:
+        # 2^28 bytes read and 2^28 bytes written per launch, 3 launches.
+        src = torch.ones(1 << 27, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
