@@ -75,9 +75,7 @@ class Runner:
         m.k2q_idx().copy_(t.arange(m.nqt, dtype=t.int32, device="cuda").expand(m.B, m.nkt, m.nqt))
 
     def build_maps(self):
-        A, ps = self.A, self.ps
-        A.pack_block_map(self.P, self.R, ps.B, ps.S, *self.ftile, out=self.fmap)
-        A.pack_block_map(self.P, self.R, ps.B, ps.S, *self.btile, out=self.bmap)
+        self.A.pack_block_maps(self.P, self.R, [self.fmap, self.bmap])
 
     def fwd(self):
         self.A.packed_attn_fwd(self.fmap, self.q, self.k, self.v, self.scale, out=(self.o, self.lse))

@@ -25,7 +25,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 PBA_OK = 0
 TILE_SKIP, TILE_PARTIAL, TILE_FULL = 0, 1, 2
 EXPORTED = ("pba_strerror", "pba_fwd_tile", "pba_bwd_tile", "pba_map_bytes", "pba_map_init",
-            "pba_pack_block_map", "pba_packed_attn_fwd", "pba_bwd_workspace_bytes", "pba_packed_attn_bwd",
+            "pba_pack_block_map", "pba_pack_block_maps", "pba_packed_attn_fwd", "pba_bwd_workspace_bytes", "pba_packed_attn_bwd",
             "pba_packed_attn_bwd_stages")
 
 
@@ -54,6 +54,10 @@ _lib.pba_map_init.restype = ctypes.c_int
 _lib.pba_pack_block_map.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
                                     ctypes.POINTER(PbaBlockMap), ctypes.c_void_p]
 _lib.pba_pack_block_map.restype = ctypes.c_int
+_lib.pba_pack_block_maps.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                     ctypes.POINTER(PbaBlockMap), ctypes.c_int, ctypes.c_void_p]
+_lib.pba_pack_block_maps.restype = ctypes.c_int
+MAX_MAPS_PER_BUILD = 4
 _lib.pba_packed_attn_fwd.argtypes = [ctypes.POINTER(PbaBlockMap)] + [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + \
     [ctypes.c_float, ctypes.c_void_p]
 _lib.pba_packed_attn_fwd.restype = ctypes.c_int
@@ -198,6 +202,21 @@ def pack_block_map(packs_dev: torch.Tensor, resp_len_dev: torch.Tensor, B: int, 
                                    resp_len_dev.data_ptr() if n_resp else None, n_resp,
                                    ctypes.byref(m.struct), _stream(stream)), "pba_pack_block_map")
     return m
+
+
+def pack_block_maps(packs_dev: torch.Tensor, resp_len_dev: torch.Tensor, maps: Sequence[BlockMap],
+                    stream=None) -> Sequence[BlockMap]:
+    """pba_pack_block_maps: build several maps of the same (B, S) together."""
+    if not 1 <= len(maps) <= MAX_MAPS_PER_BUILD:
+        raise ValueError(f"1 to {MAX_MAPS_PER_BUILD} maps per build")
+    assert packs_dev.dtype == torch.int32 and resp_len_dev.dtype == torch.int32
+    arr = (PbaBlockMap * len(maps))(*[m.struct for m in maps])
+    n_packs = packs_dev.shape[0] if packs_dev.numel() else 0
+    n_resp = resp_len_dev.numel()
+    _check(_lib.pba_pack_block_maps(packs_dev.data_ptr() if n_packs else None, n_packs,
+                                    resp_len_dev.data_ptr() if n_resp else None, n_resp, arr, len(maps),
+                                    _stream(stream)), "pba_pack_block_maps")
+    return maps
 
 
 def _bf16(x: torch.Tensor, name: str):

@@ -194,20 +194,34 @@ int pba_map_init(pba_block_map* map, void* buffer, size_t buffer_bytes, int B, i
   return PBA_OK;
 }
 
-int pba_pack_block_map(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,
-                       const pba_block_map* map, void* stream) {
-  if (!map || !map->tok_pack || !map->tok_branch || !map->tok_win || !map->cls || !map->q2k_cnt || !map->q2k_idx ||
-      !map->k2q_cnt || !map->k2q_idx || !map->totals || !map->status || !map->q_order || !map->k_order || !map->work)
-    return PBA_ERR_NULL;
+int pba_pack_block_maps(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,
+                        const pba_block_map* maps, int n_maps, void* stream) {
+  if (!maps) return PBA_ERR_NULL;
+  if (n_maps < 1 || n_maps > PBA_MAX_MAPS_PER_BUILD) return PBA_ERR_SHAPE;
   if (n_packs < 0 || n_resp_total < 0) return PBA_ERR_SHAPE;
   if ((n_packs > 0 && !packs) || (n_resp_total > 0 && !resp_len)) return PBA_ERR_NULL;
-  if (map->B < 1 || map->B > kMaxB || map->S < 1 || map->S > kMaxS) return PBA_ERR_SHAPE;
-  if (!tile_ok(map->block_m) || !tile_ok(map->block_n)) return PBA_ERR_TILE;
-  if (map->nqt != (map->S + map->block_m - 1) / map->block_m || map->nkt != (map->S + map->block_n - 1) / map->block_n)
-    return PBA_ERR_MAP;
+  for (int i = 0; i < n_maps; ++i) {
+    const pba_block_map* map = maps + i;
+    if (!map->tok_pack || !map->tok_branch || !map->tok_win || !map->cls || !map->q2k_cnt || !map->q2k_idx ||
+        !map->k2q_cnt || !map->k2q_idx || !map->totals || !map->status || !map->q_order || !map->k_order ||
+        !map->work)
+      return PBA_ERR_NULL;
+    if (map->B < 1 || map->B > kMaxB || map->S < 1 || map->S > kMaxS) return PBA_ERR_SHAPE;
+    if (map->B != maps[0].B || map->S != maps[0].S) return PBA_ERR_MAP;
+    if (!tile_ok(map->block_m) || !tile_ok(map->block_n)) return PBA_ERR_TILE;
+    if (map->nqt != (map->S + map->block_m - 1) / map->block_m ||
+        map->nkt != (map->S + map->block_n - 1) / map->block_n)
+      return PBA_ERR_MAP;
+  }
   if (int rc = device_ok()) return rc;
-  hipError_t e = pba::launch_map(packs, n_packs, resp_len, n_resp_total, *map, static_cast<hipStream_t>(stream));
+  hipError_t e = pba::launch_maps(packs, n_packs, resp_len, n_resp_total, maps, n_maps,
+                                  static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PBA_OK : PBA_ERR_DEVICE;
+}
+
+int pba_pack_block_map(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,
+                       const pba_block_map* map, void* stream) {
+  return pba_pack_block_maps(packs, n_packs, resp_len, n_resp_total, map, 1, stream);
 }
 
 int pba_packed_attn_fwd(const pba_block_map* map, const void* q, const void* k, const void* v, void* o, float* lse,

@@ -56,9 +56,9 @@ __device__ __forceinline__ void dq_tile(f32x16 (&dq)[D / 32], const bf16x8 (&qop
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int st = 0; st < C::NS; ++st) {
-      const bf16x8 kop = *(const bf16x8*)(sk + (32 * aa + l32) * C::STR + 16 * st + 8 * hi);
+      const bf16x8 kop = *(const bf16x8*)(sk + prow(32 * aa + l32) * C::STR + 16 * st + 8 * hi);
       s = mfma32(kop, qop[st], s);
-      const bf16x8 vop = *(const bf16x8*)(sv + (32 * aa + l32) * C::STR + 16 * st + 8 * hi);
+      const bf16x8 vop = *(const bf16x8*)(sv + prow(32 * aa + l32) * C::STR + 16 * st + 8 * hi);
       dp = mfma32(vop, dop[st], dp);
     }
     sched_fence();
@@ -81,7 +81,7 @@ __device__ __forceinline__ void dq_tile(f32x16 (&dq)[D / 32], const bf16x8 (&qop
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int r0 = 32 * aa + 16 * u + 4 * hi;
-        const bf16x8 kt = lds_tr8(sk, C::STR, r0, r0 + 8, 32 * e, lane);
+        const bf16x8 kt = lds_tr8p(sk, C::STR, r0, r0 + 8, 32 * e, lane);
         dq[e] = mfma32(kt, ds[u], dq[e]);
       }
     }
@@ -139,7 +139,9 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   const int kvstride = Hkv * D;
   const bf16* kb = a.k + ((int64_t)b * S * Hkv + g) * D;
   const bf16* vb = a.v + ((int64_t)b * S * Hkv + g) * D;
-  const Stager<D, C::STR> kst(tid, kvstride);
+  // One stager per staged tensor: two DMA streams sharing offset registers
+  // make the compiler wait for both before every LDS read of the tile.
+  const Stager<D, C::STR> kst(tid, kvstride), vst(tid, kvstride);
 
   f32x16 dq[C::NE];
 #pragma unroll
@@ -148,7 +150,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   if (n > 0) {
     const int k0 = min(max(list[0], 0), mp.nkt - 1) * 64;
     kst.stage(sK[0], kb + (int64_t)k0 * kvstride, S - k0);
-    kst.stage(sV[0], vb + (int64_t)k0 * kvstride, S - k0);
+    vst.stage(sV[0], vb + (int64_t)k0 * kvstride, S - k0);
   }
   wait_vmem();
   __syncthreads();
@@ -158,7 +160,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
     if (j + 1 < n) {
       const int k0 = min(max(list[j + 1], 0), mp.nkt - 1) * 64;
       kst.stage(sK[buf ^ 1], kb + (int64_t)k0 * kvstride, S - k0);
-      kst.stage(sV[buf ^ 1], vb + (int64_t)k0 * kvstride, S - k0);
+      vst.stage(sV[buf ^ 1], vb + (int64_t)k0 * kvstride, S - k0);
     }
     if (j < nfull) {
       dq_tile<D, false>(dq, qop, dop, l2, delta, sK[buf], sV[buf], a.scale_log2, 0, 0, 0, 0, lane);
@@ -212,9 +214,9 @@ __device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D
   for (int st = 0; st < C::NS; ++st) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const bf16x8 qa = *(const bf16x8*)(sq + (32 * c + l32) * C::STR + 16 * st + 8 * hi);
+      const bf16x8 qa = *(const bf16x8*)(sq + prow(32 * c + l32) * C::STR + 16 * st + 8 * hi);
       s[c] = mfma32(qa, kop[st], s[c]);
-      const bf16x8 da = *(const bf16x8*)(sdo + (32 * c + l32) * C::STR + 16 * st + 8 * hi);
+      const bf16x8 da = *(const bf16x8*)(sdo + prow(32 * c + l32) * C::STR + 16 * st + 8 * hi);
       dp[c] = mfma32(da, vop[st], dp[c]);
     }
   }
@@ -251,9 +253,9 @@ __device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int r0 = 32 * c + 16 * u + 4 * hi;
-        const bf16x8 doT = lds_tr8(sdo, C::STR, r0, r0 + 8, 32 * e, lane);
+        const bf16x8 doT = lds_tr8p(sdo, C::STR, r0, r0 + 8, 32 * e, lane);
         dvt[e] = mfma32(doT, pb[c][u], dvt[e]);
-        const bf16x8 qT = lds_tr8(sq, C::STR, r0, r0 + 8, 32 * e, lane);
+        const bf16x8 qT = lds_tr8p(sq, C::STR, r0, r0 + 8, 32 * e, lane);
         dkt[e] = mfma32(qT, db[c][u], dkt[e]);
       }
     }

@@ -37,7 +37,7 @@ struct FwdCfg {
   static constexpr int NS = D / 16;  // MFMA k-steps over the head dim
   static constexpr int NE = D / 32;  // 32-wide blocks of the head dim
   static constexpr int KSTR = D + 8;   // K tile row stride (elements)
-  static constexpr int VSTR = D + 16;  // V tile row stride (elements)
+  static constexpr int VSTR = D + 8;   // V tile row stride (elements)
 };
 
 // One key tile for one wave: S^T = K Q^T (64 keys x 32 queries), online
@@ -56,7 +56,7 @@ __device__ __forceinline__ void fwd_tile(f32x16 (&o)[D / 32], float& m, float& l
   for (int st = 0; st < C::NS; ++st) {
 #pragma unroll
     for (int aa = 0; aa < 2; ++aa) {
-      const bf16x8 kop = *(const bf16x8*)(sk + (32 * aa + l32) * C::KSTR + 16 * st + 8 * hi);
+      const bf16x8 kop = *(const bf16x8*)(sk + prow(32 * aa + l32) * C::KSTR + 16 * st + 8 * hi);
       s[aa] = mfma32(kop, qop[st], s[aa]);
     }
   }
@@ -103,7 +103,7 @@ __device__ __forceinline__ void fwd_tile(f32x16 (&o)[D / 32], float& m, float& l
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int r0 = 32 * aa + 16 * u + 4 * hi;
-        const bf16x8 vop = lds_tr8(sv, C::VSTR, r0, r0 + 8, 32 * e, lane);
+        const bf16x8 vop = lds_tr8p(sv, C::VSTR, r0, r0 + 8, 32 * e, lane);
         o[e] = mfma32(vop, p[aa][u], o[e]);
       }
     }

@@ -68,8 +68,9 @@ struct BwdArgs {
 constexpr float kLog2eHost = 1.4426950408889634f;
 
 // Launchers (return hipError_t of the launch).
-hipError_t launch_map(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,
-                      const pba_block_map& map, hipStream_t stream);
+constexpr int kMaxMapsPerBuild = PBA_MAX_MAPS_PER_BUILD;
+hipError_t launch_maps(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,
+                       const pba_block_map* maps, int n_maps, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int D, int B, hipStream_t stream);
 // Backward stages (bit mask): dQ (and Delta, LSE2), then dK / dV.
 constexpr int kBwdDq = 1, kBwdDkdv = 2, kBwdAll = 3;

@@ -36,6 +36,24 @@ __device__ __forceinline__ bf16x8 lds_tr8(const bf16* M, int stride, int r0, int
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// LDS row permutation used by every staged tile (rows of D + 8 elements):
+// inside each group of 16 rows, row 4j + i is stored at 4i + j (a 4 x 4
+// transpose; its own inverse).  With that padding, the 16 rows an A-operand
+// load reads together still fall in 16 different bank groups, and the 4
+// consecutive rows of a transpose read land 4 bank groups apart, so neither
+// access conflicts (both conflict without the permutation).  Addresses stay
+// additive in the compile-time parts, so no extra registers are needed.
+__device__ __forceinline__ int prow(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// lds_tr8 on a tile stored with prow(): r0, r1 are multiples of 4.
+__device__ __forceinline__ bf16x8 lds_tr8p(const bf16* M, int stride, int r0, int r1, int col0, int lane) {
+  const int s = lane & 15, G = lane >> 4;
+  const int col = col0 + 16 * (G & 1) + 4 * (s & 3);
+  const bf16x4 lo = lds_tr4(M + prow(r0 + (s >> 2)) * stride + col);
+  const bf16x4 hi = lds_tr4(M + prow(r1 + (s >> 2)) * stride + col);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Makes v opaque to the optimiser so that it stays in its own register for
 // as long as it lives.  Used for the per-lane offsets of LDS-DMA loads: the
 // compiler treats such a load as a store, so overwriting its offset register
@@ -59,7 +77,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16* base, in
 }
 
 // Direct buffer->LDS staging of 64 rows x D into an LDS tile with padded
-// rows of STR elements.  A wave instruction fills 1 KB of LDS in lane order,
+// rows of STR elements, row r of the tile at LDS row prow(r).  A wave instruction fills 1 KB of LDS in lane order,
 // so lane L of instruction q owns LDS bytes 1024*q + 16*L; the row and chunk
 // there decide which global chunk it fetches (lanes in a row's padding fetch
 // that row's last chunk again; the padding is never read).  The per-lane
@@ -81,8 +99,8 @@ struct Stager {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int chunk = 64 * (w * PER_WAVE + i) + lane;
-      const int r = min(chunk / (STR / 8), 63), c = min(chunk % (STR / 8), D / 8 - 1);
-      off[i] = r * row_stride_elems * 2 + 16 * c;
+      const int p = min(chunk / (STR / 8), 63), c = min(chunk % (STR / 8), D / 8 - 1);
+      off[i] = prow(p) * row_stride_elems * 2 + 16 * c;  // LDS row p holds tile row prow(p)
       pin(off[i]);
     }
   }
@@ -103,7 +121,8 @@ struct Stager {
 };
 
 // Register staging of 64 rows x D (256 threads): thread tid holds the
-// 16-byte chunks tid + 256*i, i < CH, of the tile in row-major chunk order.
+// 16-byte chunks tid + 256*i, i < CH, of the tile in row-major chunk order;
+// stored with row r at LDS row prow(r).
 // Loads go through a buffer resource whose range ends at the last valid row
 // (rows past it read as zero); the per-lane offsets are fixed, the tile's
 // position is in the (scalar) resource.
@@ -131,7 +150,7 @@ struct RegStager {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = tid + 256 * i;
-      *(u32x4*)(lds_tile + (c / (D / 8)) * STR + 8 * (c % (D / 8))) = r[i];
+      *(u32x4*)(lds_tile + prow(c / (D / 8)) * STR + 8 * (c % (D / 8))) = r[i];
     }
   }
 };

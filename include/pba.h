@@ -161,9 +161,19 @@ PBA_API int pba_map_init(pba_block_map* map, void* buffer, size_t buffer_bytes,
 /* Build the map from n_packs descriptors `packs` (device array of pba_pack)
  * and n_resp_total response lengths `resp_len` (device int32).  Validates
  * the descriptor contents on the device (map->status), then writes every
- * other field of the map.  Asynchronous on `stream`. */
+ * other field of the map (left unspecified when the status is not OK).
+ * Asynchronous on `stream`. */
 PBA_API int pba_pack_block_map(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,
                        const pba_block_map* map, void* stream);
+
+/* The same for n_maps maps of the same rows (same B and S, any tile shapes;
+ * `maps` is a host array of n_maps initialised maps, 1 <= n_maps <=
+ * PBA_MAX_MAPS_PER_BUILD), built together in four launches: the forward /
+ * dQ map and the dK / dV map of a batch are built with one call.  Each map
+ * ends up exactly as pba_pack_block_map would build it. */
+#define PBA_MAX_MAPS_PER_BUILD 4
+PBA_API int pba_pack_block_maps(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,
+                                const pba_block_map* maps, int n_maps, void* stream);
 
 /* Forward.  For every query token and q head: O = softmax(scale * Q K^T
  * restricted to the allowed keys) V, and LSE = natural log of the sum of

@@ -94,3 +94,45 @@ def test_map_is_deterministic():
     b = build_map(ps, 64, 64).to_host()
     for f in FIELDS:
         np.testing.assert_array_equal(a[f], b[f])
+
+
+def _compare_multi(ps, tiles):
+    """pba_pack_block_maps builds every map bit-exactly as the oracle does."""
+    A = api()
+    P, R = descriptor_arrays(ps)
+    pd, rd = A.descriptors_to_device(P, R)
+    maps = [A.BlockMap(ps.B, ps.S, bm, bn) for bm, bn in tiles]
+    A.pack_block_maps(pd, rd, maps)
+    for (bm, bn), m in zip(tiles, maps):
+        want = oracle.block_map(P, R, ps.B, ps.S, bm, bn)
+        got = m.to_host()
+        for f in FIELDS:
+            np.testing.assert_array_equal(got[f], want[f], err_msg=f"{f} B={ps.B} S={ps.S} tile={bm}x{bn}")
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_multi_map_build_configs(cfg):
+    ps = make_packset(cfg)
+    A = api()
+    Hq, Hkv, D = (2, 2, 64) if cfg == 1 else (32, 8, 128)
+    tiles = [A.fwd_tile(Hq, Hkv, D), A.bwd_tile(Hq, Hkv, D), (16, 32), (128, 128)]
+    say("multi map", cfg, tiles)
+    _compare_multi(ps, tiles)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_multi_map_build_random(seed):
+    rng = np.random.default_rng(3000 + seed)
+    ps = random_packset(rng, B=int(rng.integers(1, 4)), S=int(rng.integers(1, 500)), max_packs_per_row=4,
+                        max_resp=5, max_len=int(rng.integers(2, 150)))
+    say("multi map random", seed, ps.B, ps.S, len(ps.packs))
+    _compare_multi(ps, [(32, 64), (64, 128)])
+
+
+def test_work_order_large_map():
+    """More tiles per side than the order kernel sorts in LDS (2048): the
+    chunked counting-sort path, still bit-exact."""
+    rng = np.random.default_rng(77)
+    ps = random_packset(rng, B=40, S=1000, max_packs_per_row=4, max_resp=4, max_len=120)
+    say("map large order", ps.B, ps.S, len(ps.packs))
+    _compare_multi(ps, [(16, 16), (16, 64)])
