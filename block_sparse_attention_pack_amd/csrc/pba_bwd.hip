@@ -139,9 +139,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   const int kvstride = Hkv * D;
   const bf16* kb = a.k + ((int64_t)b * S * Hkv + g) * D;
   const bf16* vb = a.v + ((int64_t)b * S * Hkv + g) * D;
-  // One stager per staged tensor: two DMA streams sharing offset registers
-  // make the compiler wait for both before every LDS read of the tile.
-  const Stager<D, C::STR> kst(tid, kvstride), vst(tid, kvstride);
+  const Stager<D, C::STR> kst(tid, kvstride);  // K and V tiles have the same shape
 
   f32x16 dq[C::NE];
 #pragma unroll
@@ -150,7 +148,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   if (n > 0) {
     const int k0 = min(max(list[0], 0), mp.nkt - 1) * 64;
     kst.stage(sK[0], kb + (int64_t)k0 * kvstride, S - k0);
-    vst.stage(sV[0], vb + (int64_t)k0 * kvstride, S - k0);
+    kst.stage(sV[0], vb + (int64_t)k0 * kvstride, S - k0);
   }
   wait_vmem();
   __syncthreads();
@@ -160,7 +158,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
     if (j + 1 < n) {
       const int k0 = min(max(list[j + 1], 0), mp.nkt - 1) * 64;
       kst.stage(sK[buf ^ 1], kb + (int64_t)k0 * kvstride, S - k0);
-      vst.stage(sV[buf ^ 1], vb + (int64_t)k0 * kvstride, S - k0);
+      kst.stage(sV[buf ^ 1], vb + (int64_t)k0 * kvstride, S - k0);
     }
     if (j < nfull) {
       dq_tile<D, false>(dq, qop, dop, l2, delta, sK[buf], sV[buf], a.scale_log2, 0, 0, 0, 0, lane);
@@ -198,100 +196,128 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
 // bwd_dkdv
 // ---------------------------------------------------------------------------
 
-// One (query tile, q head) step for one wave of bwd_dkdv: 64 queries x the
-// wave's 32 keys.  Query q = q0 + 32*c + 8*(r/4) + 4*hi + r%4 sits in
-// register r of s[c]; the lane's key kj is seen by queries [kj, qend).
-template <int D, bool MASK>
-__device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D / 32], const bf16x8 (&kop)[D / 16],
-                                          const bf16x8 (&vop)[D / 16], const bf16* __restrict__ sq,
+// One (query tile, q head) step for one wave of bwd_dkdv: one 32-query half
+// of the 64-query tile (rows q0 .. q0+31 of the staged tiles) x the wave's
+// 32 keys (rows k0 .. k0+31 of the resident K / V tiles).  Query
+// q0 + 8*(r/4) + 4*hi + r%4 sits in register r of s; the lane's key kj is
+// seen by queries [kj, qend): row index x of the tile is visible iff
+// (unsigned)(x - qrel) < (unsigned)qlim (qrel = kj - first query of the tile,
+// qlim = qend - kj; qlim = -1 admits every row).
+template <int D>
+__device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D / 32], const bf16* __restrict__ sk,
+                                          const bf16* __restrict__ sv, int k0, const bf16* __restrict__ sq,
                                           const bf16* __restrict__ sdo, const float* __restrict__ sl,
-                                          const float* __restrict__ sd, float scale_log2, int qrel, int qlim,
+                                          const float* __restrict__ sd, int q0, float scale_log2, int qrel, int qlim,
                                           int lane) {
   using C = BwdCfg<D>;
   const int l32 = lane & 31, hi = lane >> 5;
-  f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+  f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
   for (int st = 0; st < C::NS; ++st) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const bf16x8 qa = *(const bf16x8*)(sq + prow(32 * c + l32) * C::STR + 16 * st + 8 * hi);
-      s[c] = mfma32(qa, kop[st], s[c]);
-      const bf16x8 da = *(const bf16x8*)(sdo + prow(32 * c + l32) * C::STR + 16 * st + 8 * hi);
-      dp[c] = mfma32(da, vop[st], dp[c]);
-    }
+    const bf16x8 qa = *(const bf16x8*)(sq + prow(q0 + l32) * C::STR + 16 * st + 8 * hi);
+    const bf16x8 kb = *(const bf16x8*)(sk + prow(k0 + l32) * C::STR + 16 * st + 8 * hi);
+    s = mfma32(qa, kb, s);
+    const bf16x8 da = *(const bf16x8*)(sdo + prow(q0 + l32) * C::STR + 16 * st + 8 * hi);
+    const bf16x8 vb = *(const bf16x8*)(sv + prow(k0 + l32) * C::STR + 16 * st + 8 * hi);
+    dp = mfma32(da, vb, dp);
   }
   sched_fence();
-  bf16x8 pb[2][2], db[2][2];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int rg = 0; rg < 4; ++rg) {
+    const int qr = q0 + 8 * rg + 4 * hi;  // rows qr .. qr+3 in registers 4*rg .. 4*rg+3
+    const f32x4 lv = *(const f32x4*)(sl + qr);
+    const f32x4 dv = *(const f32x4*)(sd + qr);
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int qr = 32 * c + 8 * rg + 4 * hi;  // rows qr .. qr+3 in registers 4*rg .. 4*rg+3
-      const f32x4 lv = *(const f32x4*)(sl + qr);
-      const f32x4 dv = *(const f32x4*)(sd + qr);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r = 4 * rg + t;
-        float p = fast_exp2(__builtin_fmaf(s[c][r], scale_log2, -lv[t]));
-        if (MASK) p = (unsigned)(qr + t - qrel) < (unsigned)qlim ? p : 0.f;
-        s[c][r] = p;
-        dp[c][r] = p * (dp[c][r] - dv[t]);
-      }
+    for (int t = 0; t < 4; ++t) {
+      const int r = 4 * rg + t;
+      float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -lv[t]));
+      p = (unsigned)(qr + t - qrel) < (unsigned)qlim ? p : 0.f;
+      s[r] = p;
+      dp[r] = p * (dp[r] - dv[t]);
     }
-    pb[c][0] = pack8(s[c], 0);
-    pb[c][1] = pack8(s[c], 8);
-    db[c][0] = pack8(dp[c], 0);
-    db[c][1] = pack8(dp[c], 8);
   }
+  const bf16x8 pb[2] = {pack8(s, 0), pack8(s, 8)};
+  const bf16x8 db[2] = {pack8(dp, 0), pack8(dp, 8)};
   sched_fence();
-  // dV^T += dO^T P and dK^T += Q^T dS (reduction over queries, in the
-  // register order of P / dS).
+  // dV^T += dO^T P and dK^T += Q^T dS (reduction over the 32 queries, in
+  // the register order of P / dS).
 #pragma unroll
   for (int e = 0; e < C::NE; ++e) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int r0 = 32 * c + 16 * u + 4 * hi;
-        const bf16x8 doT = lds_tr8p(sdo, C::STR, r0, r0 + 8, 32 * e, lane);
-        dvt[e] = mfma32(doT, pb[c][u], dvt[e]);
-        const bf16x8 qT = lds_tr8p(sq, C::STR, r0, r0 + 8, 32 * e, lane);
-        dkt[e] = mfma32(qT, db[c][u], dkt[e]);
-      }
+    for (int u = 0; u < 2; ++u) {
+      const int r0 = q0 + 16 * u + 4 * hi;
+      const bf16x8 doT = lds_tr8p(sdo, C::STR, r0, r0 + 8, 32 * e, lane);
+      dvt[e] = mfma32(doT, pb[u], dvt[e]);
+      const bf16x8 qT = lds_tr8p(sq, C::STR, r0, r0 + 8, 32 * e, lane);
+      dkt[e] = mfma32(qT, db[u], dkt[e]);
     }
   }
 }
 
+// End of bwd_dkdv: the wave of query half 1 puts its partial sums in its
+// lane-private LDS slot, the partner wave (half 0) adds them to its own and
+// writes scale * sum as bf16 (lane: head dims 32e + 8*(r/4) + 4*hi + r%4).
 template <int D>
-__global__ void __launch_bounds__(256, 1) bwd_dkdv(BwdArgs a) {
+__device__ __forceinline__ void pair_sum_store(const f32x16 (&acc)[D / 32], float* slot, int qh, bool valid,
+                                               bf16* out, float scale) {
+  constexpr int NE = D / 32;
+  if (qh == 1) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg)
+        *(f32x4*)(slot + 16 * e + 4 * rg) =
+            f32x4{acc[e][4 * rg], acc[e][4 * rg + 1], acc[e][4 * rg + 2], acc[e][4 * rg + 3]};
+  }
+  __syncthreads();
+  if (qh == 0 && valid) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const f32x4 o = *(const f32x4*)(slot + 16 * e + 4 * rg);
+        bf16x4 v;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = (bf16)((acc[e][4 * rg + t] + o[t]) * scale);
+        *(bf16x4*)(out + 32 * e + 8 * rg) = v;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// 8 waves, 128 keys: wave w owns keys 32*(w%4) .. +31 and the query half
+// w/4 of every 64-query step.  K and V of the 128 keys stay in LDS for the
+// whole kernel (B operands read per step); Q, dO, LSE2 and Delta tiles are
+// staged by direct loads into a double buffer.  The two waves that share
+// keys sum their partial dK / dV through LDS at the end.
+template <int D>
+__global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(1024))) bf16 sQ[2][64 * C::STR];
-  __shared__ __attribute__((aligned(1024))) bf16 sDO[2][64 * C::STR];
+  constexpr int TQ = 64 * C::STR;  // elements of one staged 64-row tile
+  __shared__ __attribute__((aligned(1024))) bf16 sK[128 * C::STR];
+  __shared__ __attribute__((aligned(1024))) bf16 sV[128 * C::STR];
+  // Q and dO double buffers (indexed [buf] / [buf ^ 1], which lets the
+  // compiler see that the tile being read and the one being loaded never
+  // overlap).  After the loop they hold the exchange of partial sums: key
+  // blocks 0-1 in sQ, 2-3 in sDO (2 waves x 64 lanes x D/2 fp32 each).
+  __shared__ __attribute__((aligned(1024))) bf16 sQ[2][TQ];
+  __shared__ __attribute__((aligned(1024))) bf16 sDO[2][TQ];
+  static_assert(2 * TQ * sizeof(bf16) >= 2 * 64 * (D / 2) * sizeof(float), "exchange must fit a staging array");
   __shared__ __attribute__((aligned(16))) float sL[2][64], sD[2][64];
 
   const MapView& mp = a.kmap;
   if (cptr(mp.status)[0] != 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hi = lane >> 5;
+  const int l32 = lane & 31;
+  const int kb = w & 3, qh = w >> 2;  // key block, query half
   const int Hkv = a.Hkv, G = a.G, S = a.S, Hq = a.Hq;
   const int item = cptr(mp.k_order)[blockIdx.x / Hkv];
   const int g = blockIdx.x % Hkv;
   const int b = item / mp.nkt, kt = item % mp.nkt;
-  const int kj = kt * 128 + 32 * w + l32;  // this lane's key
-  const int kc = min(kj, S - 1);
-
-  // K and V of the lane's key as B operands of S = Q K^T and dP = dO V^T.
-  bf16x8 kop[C::NS], vop[C::NS];
-  {
-    const int64_t off = (((int64_t)b * S + kc) * Hkv + g) * D + 8 * hi;
-#pragma unroll
-    for (int st = 0; st < C::NS; ++st) {
-      kop[st] = *(const bf16x8*)(a.k + off + 16 * st);
-      vop[st] = *(const bf16x8*)(a.v + off + 16 * st);
-    }
-  }
-  const int qend = kj < S ? reinterpret_cast<const int4*>(mp.tok_win)[(int64_t)b * S + kc].w : kj;
+  const int kj = kt * 128 + 32 * kb + l32;  // this lane's key
+  const int qend = kj < S ? reinterpret_cast<const int4*>(mp.tok_win)[(int64_t)b * S + kj].w : kj;
 
   const int64_t lrow = (int64_t)b * mp.nkt + kt;
   const cint_ptr cnt = cptr(mp.k2q_cnt) + lrow * 2;
@@ -299,84 +325,69 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv(BwdArgs a) {
   const int nfull = min(max(cnt[0], 0), n);
   const cint_ptr list = cptr(mp.k2q_idx) + lrow * mp.nqt;
 
-  // The next step's Q and dO tiles and its 64 LSE2 / Delta values are
-  // loaded into registers while the current step computes, and written to
-  // the other LDS buffer after the current step's last LDS read.
-  const int qstride = Hq * D;
-  using Reg = RegStager<D, C::STR>;
-  const Reg qst(tid, qstride);
-  u32x4 rq[Reg::CH], rdo[Reg::CH];
-  float rl = 0.f, rd = 0.f;
-  auto load_step = [&](int i, int hh) {
+  const int kvstride = Hkv * D, qstride = Hq * D;
+  const Stager<D, C::STR, 128, 8> kst(tid, kvstride);  // K and V
+  const Stager<D, C::STR, 64, 8> qst(tid, qstride);    // Q and dO
+  int lane4 = lane * 4;
+  pin(lane4);
+  {
+    const int64_t koff = ((int64_t)b * S + kt * 128) * kvstride + (int64_t)g * D;
+    kst.stage(sK, a.k + koff, S - kt * 128);
+    kst.stage(sV, a.v + koff, S - kt * 128);
+  }
+  auto stage = [&](int i, int hh, int buf) {
     const int qt = min(max(list[i], 0), mp.nqt - 1), h = g * G + hh;
     const int64_t toff = ((int64_t)b * S + qt * 64) * qstride + (int64_t)h * D;
-    qst.load(rq, a.q + toff, S - qt * 64);
-    qst.load(rdo, a.dout + toff, S - qt * 64);
-    if (tid < 64) {
-      const int q = qt * 64 + tid;
-      const int64_t ro = ((int64_t)b * Hq + h) * S + min(q, S - 1);
-      rl = q < S ? a.lse2[ro] : 0.f;
-      rd = q < S ? a.delta[ro] : 0.f;
-    }
-  };
-  auto store_step = [&](int buf) {
-    Reg::store(sQ[buf], rq, tid);
-    Reg::store(sDO[buf], rdo, tid);
-    if (tid < 64) {
-      sL[buf][tid] = rl;
-      sD[buf][tid] = rd;
-    }
+    qst.stage(sQ[buf], a.q + toff, S - qt * 64);
+    qst.stage(sDO[buf], a.dout + toff, S - qt * 64);
+    const int64_t roff = ((int64_t)b * Hq + h) * S + qt * 64;
+    if (w == 0) buffer_lds_dword(a.lse2 + roff, S - qt * 64, &sL[buf][0], lane4);
+    if (w == 1) buffer_lds_dword(a.delta + roff, S - qt * 64, &sD[buf][0], lane4);
   };
 
   f32x16 dkt[C::NE], dvt[C::NE];
 #pragma unroll
   for (int e = 0; e < C::NE; ++e) dkt[e] = dvt[e] = f32x16{};
 
-  if (n > 0) {
-    load_step(0, 0);
-    store_step(0);
-  }
+  // The resident K / V tiles are read through pointers the compiler cannot
+  // fold to constant addresses, so that those reads keep the alias scope of
+  // dkdv_step's restrict parameters (an LDS read without one waits for
+  // every outstanding global->LDS load, i.e. for the next step's tiles).
+  const bf16* skp = opaque_lds(sK);
+  const bf16* svp = opaque_lds(sV);
+  if (n > 0) stage(0, 0, 0);
+  wait_vmem();
   __syncthreads();
   int buf = 0;
   for (int i = 0; i < n; ++i) {
     const int qt = min(max(list[i], 0), mp.nqt - 1);
     const bool masked = i >= nfull;
     for (int hh = 0; hh < G; ++hh) {
-      const bool next_same = hh + 1 < G, next_tile = !next_same && i + 1 < n;
-      if (next_same) load_step(i, hh + 1);
-      else if (next_tile) load_step(i + 1, 0);
-      if (!masked) {
-        dkdv_step<D, false>(dkt, dvt, kop, vop, sQ[buf], sDO[buf], sL[buf], sD[buf], a.scale_log2, 0, 0, lane);
-      } else {
-        dkdv_step<D, true>(dkt, dvt, kop, vop, sQ[buf], sDO[buf], sL[buf], sD[buf], a.scale_log2,
-                           kj - qt * 64, qend - kj, lane);
-      }
-      // The other buffer was last read one step ago (before the barrier).
-      if (next_same || next_tile) store_step(buf ^ 1);
+      // Prefetch the next step into the other buffer (last read one step ago).
+      if (hh + 1 < G) stage(i, hh + 1, buf ^ 1);
+      else if (i + 1 < n) stage(i + 1, 0, buf ^ 1);
+      // One code path for full and partial tiles: a full tile gets a
+      // window that admits every query.
+      const int qrel = masked ? kj - qt * 64 : 0;
+      const int qlim = masked ? qend - kj : -1;
+      dkdv_step<D>(dkt, dvt, skp, svp, 32 * kb, sQ[buf], sDO[buf], sL[buf], sD[buf], 32 * qh, a.scale_log2, qrel, qlim,
+                   lane);
+      wait_vmem();
       __syncthreads();
       buf ^= 1;
     }
   }
 
-  // dK = scale * (dK^T)^T, dV = (dV^T)^T.  Lane: key kj, head dims
+  // Sum the two query halves: the waves of half 1 hand their partial dK^T,
+  // then dV^T, to their partners through LDS (lane-private slots in the
+  // Q / dO staging area), which write the result.  Lane: key kj, head dims
   // 32e + 8*(r/4) + 4*hi + r%4.
-  if (kj < S) {
-    const int64_t off = (((int64_t)b * S + kj) * Hkv + g) * D + 4 * hi;
-#pragma unroll
-    for (int e = 0; e < C::NE; ++e) {
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        bf16x4 vk, vv;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          vk[t] = (bf16)(dkt[e][4 * rg + t] * a.scale);
-          vv[t] = (bf16)dvt[e][4 * rg + t];
-        }
-        *(bf16x4*)(a.dk + off + 32 * e + 8 * rg) = vk;
-        *(bf16x4*)(a.dv + off + 32 * e + 8 * rg) = vv;
-      }
-    }
-  }
+  float* xch = reinterpret_cast<float*>(kb < 2 ? &sQ[0][0] : &sDO[0][0]);
+  const int hi = lane >> 5;
+  const int64_t off = (((int64_t)b * S + min(kj, S - 1)) * Hkv + g) * D + 4 * hi;
+  float* slot = xch + ((kb & 1) * 64 + lane) * (D / 2);
+  pair_sum_store<D>(dkt, slot, qh, kj < S, a.dk + off, a.scale);
+  pair_sum_store<D>(dvt, slot, qh, kj < S, a.dv + off, 1.f);
 }
 
 template <int D>
@@ -390,7 +401,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, int stages, hipStream_t stream) {
   }
   if (stages & kBwdDkdv) {
     const unsigned nblk = (unsigned)((int64_t)a.B * a.kmap.nkt * a.Hkv);
-    bwd_dkdv<D><<<nblk, 256, 0, stream>>>(a);
+    bwd_dkdv<D><<<nblk, 512, 0, stream>>>(a);
   }
   return hipGetLastError();
 }

@@ -154,7 +154,7 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   const bf16* kb = a.k + ((int64_t)b * S * Hkv + g) * D;
   const bf16* vb = a.v + ((int64_t)b * S * Hkv + g) * D;
   const Stager<D, C::KSTR> kst(tid, kvstride);
-  const Stager<D, C::VSTR> vst(tid, kvstride);
+  static_assert(C::KSTR == C::VSTR, "K and V tiles share one stager");
 
   float m = kNegInf, l = 0.f;
   f32x16 o[C::NE];
@@ -164,7 +164,7 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   if (n > 0) {
     const int k0 = min(max(list[0], 0), mp.nkt - 1) * 64;
     kst.stage(sK[0], kb + (int64_t)k0 * kvstride, S - k0);
-    vst.stage(sV[0], vb + (int64_t)k0 * kvstride, S - k0);
+    kst.stage(sV[0], vb + (int64_t)k0 * kvstride, S - k0);
   }
   wait_vmem();
   __syncthreads();
@@ -175,7 +175,7 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
     if (j + 1 < n) {
       const int k0 = min(max(list[j + 1], 0), mp.nkt - 1) * 64;
       kst.stage(sK[buf ^ 1], kb + (int64_t)k0 * kvstride, S - k0);
-      vst.stage(sV[buf ^ 1], vb + (int64_t)k0 * kvstride, S - k0);
+      kst.stage(sV[buf ^ 1], vb + (int64_t)k0 * kvstride, S - k0);
     }
     if (j < nfull) {
       fwd_tile<D, false>(o, m, l, qop, sK[buf], sV[buf], a.scale_log2, 0, 0, 0, 0, lane);

@@ -54,12 +54,41 @@ __device__ __forceinline__ bf16x8 lds_tr8p(const bf16* M, int stride, int r0, in
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// One direct buffer->LDS load: each lane fetches SIZE bytes (4 or 16) at
+// byte offset voff of the resource and the wave writes them to LDS at
+// lds_dst + SIZE * lane (lds_dst wave-uniform).  Issued as inline assembly
+// so that the compiler does not attach its own completion waits to later
+// LDS reads (it cannot tell which LDS range the load writes and would make
+// every read wait for it).  The caller orders the load: it never reads the
+// destination before an explicit wait_vmem() and a barrier, and never
+// loads into a buffer that another wave may still be reading.
+template <int SIZE>
+__device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t rs, const void* lds_dst, int voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const unsigned m0 = (unsigned)(uintptr_t)(PBA_LDS const void*)lds_dst;
+  if (SIZE == 16)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+                 "s"(m0)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+                 "s"(m0)
+                 : "memory", "m0");
+#endif
+}
+
 // Makes v opaque to the optimiser so that it stays in its own register for
-// as long as it lives.  Used for the per-lane offsets of LDS-DMA loads: the
-// compiler treats such a load as a store, so overwriting its offset register
-// while it is in flight costs a wait for all outstanding loads, and a
-// rematerialised (recomputed) offset would be overwritten right away.
+// as long as it lives (used for the per-lane offsets of the tile loads, which
+// would otherwise be recomputed before every load).
 __device__ __forceinline__ void pin(int& v) { asm volatile("" : "+v"(v)); }
+
+// p plus an offset of 0 that the optimiser cannot see through.
+template <typename T>
+__device__ __forceinline__ T* opaque_lds(T* p) {
+  int z = 0;
+  asm volatile("" : "+s"(z));
+  return p + z;
+}
 
 // Read-only map arrays through the constant address space, so that
 // wave-uniform indices become scalar loads (they then never wait behind the
@@ -76,19 +105,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16* base, in
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nbytes, 0x00020000);
 }
 
-// Direct buffer->LDS staging of 64 rows x D into an LDS tile with padded
-// rows of STR elements, row r of the tile at LDS row prow(r).  A wave instruction fills 1 KB of LDS in lane order,
+// Direct buffer->LDS staging of ROWS rows x D into an LDS tile with padded
+// rows of STR elements, row r of the tile at LDS row prow(r), by a
+// workgroup of NWAVES waves.  A wave instruction fills 1 KB of LDS in lane order,
 // so lane L of instruction q owns LDS bytes 1024*q + 16*L; the row and chunk
 // there decide which global chunk it fetches (lanes in a row's padding fetch
 // that row's last chunk again; the padding is never read).  The per-lane
 // offsets are fixed for the whole kernel; the tile's position goes into the
 // (scalar) buffer resource, whose range ends at the last valid row, so rows
 // past the end of the sequence read as zeros.
-template <int D, int STR>
+template <int D, int STR, int ROWS = 64, int NWAVES = 4>
 struct Stager {
-  static constexpr int NI = 64 * STR * 2 / 1024;  // 1 KB instructions per tile
-  static constexpr int PER_WAVE = (NI + 3) / 4;
-  static_assert((64 * STR * 2) % 1024 == 0, "tile must be whole 1 KB blocks");
+  static constexpr int NI = ROWS * STR * 2 / 1024;  // 1 KB instructions per tile
+  static constexpr int PER_WAVE = (NI + NWAVES - 1) / NWAVES;
+  static_assert((ROWS * STR * 2) % 1024 == 0, "tile must be whole 1 KB blocks");
   int off[PER_WAVE];  // byte offset of this lane's chunk from the tile's first row
   int w;
   int row_stride;
@@ -99,13 +129,13 @@ struct Stager {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int chunk = 64 * (w * PER_WAVE + i) + lane;
-      const int p = min(chunk / (STR / 8), 63), c = min(chunk % (STR / 8), D / 8 - 1);
+      const int p = min(chunk / (STR / 8), ROWS - 1), c = min(chunk % (STR / 8), D / 8 - 1);
       off[i] = prow(p) * row_stride_elems * 2 + 16 * c;  // LDS row p holds tile row prow(p)
       pin(off[i]);
     }
   }
-  // Rows [0, 64) of the tile starting at `tile`, of which `rows` (>= 1) are
-  // valid, into lds_tile.
+  // Rows [0, ROWS) of the tile starting at `tile`, of which `rows` (>= 1)
+  // are valid, into lds_tile.
   // (The builtin exists only for the device; the host pass, which never runs
   // this, must not instantiate it or it drops the kernels' host stubs.)
   __device__ __forceinline__ void stage(bf16* lds_tile, const bf16* tile, int rows) const {
@@ -114,7 +144,7 @@ struct Stager {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int q = w * PER_WAVE + i;
-      if (q < NI) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (PBA_LDS void*)(lds_tile + 512 * q), 16, off[i], 0, 0, 0);
+      if (q < NI) dma_to_lds<16>(rs, lds_tile + 512 * q, off[i]);
     }
 #endif
   }
@@ -161,7 +191,7 @@ struct RegStager {
 __device__ __forceinline__ void buffer_lds_dword(const float* src, int n, float* dst, int lane4) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, n * 4, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (PBA_LDS void*)dst, 4, lane4, 0, 0, 0);
+  dma_to_lds<4>(rs, dst, lane4);
 #endif
 }
 
