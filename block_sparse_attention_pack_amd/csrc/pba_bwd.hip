@@ -22,6 +22,8 @@
 // dQ and dK / dV are each owned by exactly one workgroup, so they are written
 // once, in bf16, with no accumulator pass (fp32 atomics into a dQ buffer are
 // capped by the L2 atomic rate far below the MFMA rate at these shapes).
+#include <type_traits>
+
 #include "pba_tile.h"
 
 namespace pba {
@@ -152,7 +154,11 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   }
   wait_vmem();
   __syncthreads();
-  for (int j = 0; j < n; ++j) {
+  // One visit: the next tile's loads go into the other buffer, then this
+  // tile's math.  Full tiles precede partial ones in the list; a loop for
+  // each keeps the dQ accumulators in place (two paths merging inside one
+  // loop body would copy every accumulator per tile).
+  auto visit = [&](int j, auto masked) {
     const int kt = min(max(list[j], 0), mp.nkt - 1);
     const int buf = j & 1;
     if (j + 1 < n) {
@@ -160,16 +166,19 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
       kst.stage(sK[buf ^ 1], kb + (int64_t)k0 * kvstride, S - k0);
       kst.stage(sV[buf ^ 1], vb + (int64_t)k0 * kvstride, S - k0);
     }
-    if (j < nfull) {
-      dq_tile<D, false>(dq, qop, dop, l2, delta, sK[buf], sV[buf], a.scale_log2, 0, 0, 0, 0, lane);
-    } else {
+    if constexpr (decltype(masked)::value) {
       const int jb = kt * 64 + 4 * hi;
       dq_tile<D, true>(dq, qop, dop, l2, delta, sK[buf], sV[buf], a.scale_log2, qi - jb, wlo - jb, jb - wplo,
                        wphi - wplo, lane);
+    } else {
+      dq_tile<D, false>(dq, qop, dop, l2, delta, sK[buf], sV[buf], a.scale_log2, 0, 0, 0, 0, lane);
     }
     wait_vmem();
     __syncthreads();
-  }
+  };
+  int j = 0;
+  for (; j < nfull; ++j) visit(j, std::false_type{});
+  for (; j < n; ++j) visit(j, std::true_type{});
 
   // (Delta and LSE2 are stored only now: a store still in flight when the
   // loop reuses its data registers would make every tile wait for memory.)

@@ -25,6 +25,8 @@
 // through buffer resources whose range ends at the row's last token, so key
 // rows past it read as zeros; they only ever meet masked (partial-tile)
 // scores, whose probability is exactly 0.
+#include <type_traits>
+
 #include "pba_tile.h"
 
 namespace pba {
@@ -113,8 +115,14 @@ __device__ __forceinline__ void fwd_tile(f32x16 (&o)[D / 32], float& m, float& l
 template <int D, int WGH>
 __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(1024))) bf16 sK[2][64 * C::KSTR];
-  __shared__ __attribute__((aligned(1024))) bf16 sV[2][64 * C::VSTR];
+  static_assert(C::KSTR == C::VSTR, "K and V tiles share one stager");
+  constexpr int T = 64 * C::KSTR;  // elements of one K or V tile
+  // K/V double buffers: K(0) V(0) K(1) V(1).  The workgroup's Q block is
+  // first staged in the second pair and its O block leaves through LDS.
+  __shared__ __attribute__((aligned(1024))) bf16 lds[4 * T];
+  constexpr int R = 32 * (4 / WGH);  // query rows of the workgroup
+  using Blk = RowBlock<R, WGH * D * 2>;
+  static_assert(Blk::BYTES <= 2 * T * 2 && R * Blk::LSTR <= 4 * T * 2, "Q / O block fits the LDS buffers");
 
   const MapView& mp = a.map;
   if (cptr(mp.status)[0] != 0) return;
@@ -122,25 +130,20 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
   const int l32 = lane & 31, hi = lane >> 5;
   const int nhg = a.Hq / WGH;
-  const int item = cptr(mp.q_order)[blockIdx.x / nhg];  // b * nqt + qt, longest lists first
+  // b * nqt + qt, longest lists first (clamped like every map read below)
+  const int item = min(max(cptr(mp.q_order)[blockIdx.x / nhg], 0), mp.B * mp.nqt - 1);
   const int b = item / mp.nqt, qt = item % mp.nqt;
-  const int h = (blockIdx.x % nhg) * WGH + (w % WGH);
+  const int h0 = (blockIdx.x % nhg) * WGH;
+  const int hw = w % WGH, qb = w / WGH;  // this wave's head and 32-query block
+  const int h = h0 + hw;
   const int g = h / a.G;
   const int S = a.S, Hq = a.Hq, Hkv = a.Hkv;
-  const int qi = qt * (32 * (4 / WGH)) + (w / WGH) * 32 + l32;  // this lane's query
-
-  // Q^T as the B operand: lane holds query qi, head dims 16*st + 8*hi + 0..7.
-  bf16x8 qop[C::NS];
-  int wlo, wplo, wphi;
-  {
-    const bf16* qrow = a.q + (((int64_t)b * S + min(qi, S - 1)) * Hq + h) * D + 8 * hi;
-#pragma unroll
-    for (int st = 0; st < C::NS; ++st) qop[st] = *(const bf16x8*)(qrow + 16 * st);
-    const int4 wv = reinterpret_cast<const int4*>(mp.tok_win)[(int64_t)b * S + min(qi, S - 1)];
-    wlo = qi < S ? wv.x : qi + 1;
-    wplo = qi < S ? wv.y : 0;
-    wphi = qi < S ? wv.z : 0;
-  }
+  const int q0 = qt * R;
+  const int qi = q0 + qb * 32 + l32;  // this lane's query
+  const int qrows = min(R, S - q0);
+  const int qrow_bytes = Hq * D * 2;
+  char* const qo_lds = (char*)lds;  // the Q block (second buffer pair) and later the O block
+  char* const q_lds = qo_lds + 2 * T * 2;
 
   const int64_t lrow = (int64_t)b * mp.nqt + qt;
   // Counts are clamped so that even a corrupted map cannot index outside
@@ -154,44 +157,72 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   const bf16* kb = a.k + ((int64_t)b * S * Hkv + g) * D;
   const bf16* vb = a.v + ((int64_t)b * S * Hkv + g) * D;
   const Stager<D, C::KSTR> kst(tid, kvstride);
-  static_assert(C::KSTR == C::VSTR, "K and V tiles share one stager");
+  auto sK = [&](int buf) { return lds + (2 * buf) * T; };
+  auto sV = [&](int buf) { return lds + (2 * buf + 1) * T; };
+
+  // Prologue: the Q block and the first K/V tile, all as direct loads.
+  Blk::template load<4>(q_lds, a.q + ((int64_t)b * S + q0) * Hq * D + (int64_t)h0 * D, qrows, qrow_bytes, w, lane);
+  if (n > 0) {
+    const int k0 = min(max(list[0], 0), mp.nkt - 1) * 64;
+    kst.stage(sK(0), kb + (int64_t)k0 * kvstride, S - k0);
+    kst.stage(sV(0), vb + (int64_t)k0 * kvstride, S - k0);
+  }
+  int wlo, wplo, wphi;
+  {
+    const int4 wv = reinterpret_cast<const int4*>(mp.tok_win)[(int64_t)b * S + min(qi, S - 1)];
+    wlo = qi < S ? wv.x : qi + 1;
+    wplo = qi < S ? wv.y : 0;
+    wphi = qi < S ? wv.z : 0;
+  }
+  wait_vmem();
+  __syncthreads();
+  // Q^T as the B operand: lane holds query qi, head dims 16*st + 8*hi + 0..7.
+  bf16x8 qop[C::NS];
+  {
+    const char* qr = q_lds + (qb * 32 + l32) * Blk::LSTR + hw * D * 2 + 16 * hi;
+#pragma unroll
+    for (int st = 0; st < C::NS; ++st) qop[st] = *(const bf16x8*)(qr + 32 * st);
+  }
+  __syncthreads();  // the second buffer pair is free again
 
   float m = kNegInf, l = 0.f;
   f32x16 o[C::NE];
 #pragma unroll
   for (int e = 0; e < C::NE; ++e) o[e] = f32x16{};
 
-  if (n > 0) {
-    const int k0 = min(max(list[0], 0), mp.nkt - 1) * 64;
-    kst.stage(sK[0], kb + (int64_t)k0 * kvstride, S - k0);
-    kst.stage(sV[0], vb + (int64_t)k0 * kvstride, S - k0);
-  }
-  wait_vmem();
-  __syncthreads();
-  for (int j = 0; j < n; ++j) {
+  // One visit: start the next tile's loads into the other buffer (last read
+  // in the previous visit, which every wave has left), then this tile's math.
+  auto visit = [&](int j, auto masked) {
     const int kt = min(max(list[j], 0), mp.nkt - 1);
     const int buf = j & 1;
-    // The other buffer was last read in step j-1, which every wave has left.
     if (j + 1 < n) {
       const int k0 = min(max(list[j + 1], 0), mp.nkt - 1) * 64;
-      kst.stage(sK[buf ^ 1], kb + (int64_t)k0 * kvstride, S - k0);
-      kst.stage(sV[buf ^ 1], vb + (int64_t)k0 * kvstride, S - k0);
+      kst.stage(sK(buf ^ 1), kb + (int64_t)k0 * kvstride, S - k0);
+      kst.stage(sV(buf ^ 1), vb + (int64_t)k0 * kvstride, S - k0);
     }
-    if (j < nfull) {
-      fwd_tile<D, false>(o, m, l, qop, sK[buf], sV[buf], a.scale_log2, 0, 0, 0, 0, lane);
-    } else {
+    if constexpr (decltype(masked)::value) {
       const int jb = kt * 64 + 4 * hi;
-      fwd_tile<D, true>(o, m, l, qop, sK[buf], sV[buf], a.scale_log2, qi - jb, wlo - jb, jb - wplo, wphi - wplo, lane);
+      fwd_tile<D, true>(o, m, l, qop, sK(buf), sV(buf), a.scale_log2, qi - jb, wlo - jb, jb - wplo, wphi - wplo, lane);
+    } else {
+      fwd_tile<D, false>(o, m, l, qop, sK(buf), sV(buf), a.scale_log2, 0, 0, 0, 0, lane);
     }
     wait_vmem();
     __syncthreads();
-  }
+  };
+  // Full tiles come first in the list, then partial ones.  Two loops rather
+  // than a branch in one keep each loop's accumulators in place (a merge of
+  // two paths inside one loop body costs a copy of every accumulator).
+  int j = 0;
+  for (; j < nfull; ++j) visit(j, std::false_type{});
+  for (; j < n; ++j) visit(j, std::true_type{});
 
-  // Epilogue: normalise, write O (bf16) and LSE (natural log).
+  // Epilogue: normalise; O (bf16) goes through LDS (free after the last
+  // barrier) so that its rows leave as whole contiguous segments; LSE in
+  // natural log.
   const float lt = l + wave_half_swap(l);
-  if (qi < S) {
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    bf16* orow = a.o + (((int64_t)b * S + qi) * Hq + h) * D + 4 * hi;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  {
+    char* orow = qo_lds + (qb * 32 + l32) * Blk::LSTR + hw * D * 2 + 8 * hi;
 #pragma unroll
     for (int e = 0; e < C::NE; ++e) {
 #pragma unroll
@@ -199,11 +230,13 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
         bf16x4 v;
 #pragma unroll
         for (int t = 0; t < 4; ++t) v[t] = (bf16)(o[e][4 * rg + t] * inv);
-        *(bf16x4*)(orow + 32 * e + 8 * rg) = v;
+        *(bf16x4*)(orow + 2 * (32 * e + 8 * rg)) = v;
       }
     }
-    if (hi == 0) a.lse[((int64_t)b * Hq + h) * S + qi] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
   }
+  if (qi < S && hi == 0) a.lse[((int64_t)b * Hq + h) * S + qi] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+  __syncthreads();
+  Blk::template store<256>(a.o + ((int64_t)b * S + q0) * Hq * D + (int64_t)h0 * D, qo_lds, qrows, qrow_bytes, tid);
 }
 
 template <int D>

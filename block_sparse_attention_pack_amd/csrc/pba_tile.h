@@ -185,6 +185,49 @@ struct RegStager {
   }
 };
 
+// A workgroup's block of R rows x RB bytes that are contiguous within a row
+// in HBM (e.g. one query tile's rows over the workgroup's adjacent heads),
+// rows `row_bytes` apart, mirrored in LDS with rows padded by 16 bytes.
+// Both directions move whole 16-byte chunks with consecutive lanes on
+// consecutive addresses, so every wave instruction covers full row segments.
+template <int R, int RB>
+struct RowBlock {
+  static_assert(RB % 16 == 0, "rows are whole 16-byte chunks");
+  static constexpr int LSTR = RB + 16;            // LDS row stride (bytes)
+  static constexpr int CH = LSTR / 16;            // chunks per LDS row, pad included
+  static constexpr int NI = (R * CH + 63) / 64;   // DMA wave instructions for the block
+  static constexpr int BYTES = NI * 1024;         // LDS bytes written by load()
+
+  // HBM -> LDS with direct loads (wave w of NWAVES issues instructions
+  // w, w + NWAVES, ...); rows >= rows_valid (>= 1) read as zeros.  The
+  // caller waits (wait_vmem + barrier) before reading the block.
+  template <int NWAVES>
+  __device__ __forceinline__ static void load(char* lds, const void* g, int rows_valid, int row_bytes, int w,
+                                              int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int nbytes = (rows_valid - 1) * row_bytes + RB;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)g, (short)0, nbytes, 0x00020000);
+    for (int i = w; i < NI; i += NWAVES) {
+      const int c = 64 * i + lane;
+      const int p = min(c / CH, R - 1), cc = min(c % CH, RB / 16 - 1);
+      dma_to_lds<16>(rs, lds + 1024 * i, p * row_bytes + 16 * cc);
+    }
+#endif
+  }
+  // LDS -> HBM by NT threads, rows >= rows_valid skipped.
+  template <int NT>
+  __device__ __forceinline__ static void store(void* g, const char* lds, int rows_valid, int row_bytes, int tid) {
+    constexpr int RC = RB / 16, TOTAL = R * RC;
+#pragma unroll
+    for (int i = 0; i < (TOTAL + NT - 1) / NT; ++i) {
+      const int c = tid + NT * i;
+      const int p = c / RC, cc = c % RC;
+      if ((TOTAL % NT == 0 || c < TOTAL) && p < rows_valid)
+        *(u32x4*)((char*)g + (int64_t)p * row_bytes + 16 * cc) = *(const u32x4*)(lds + p * LSTR + 16 * cc);
+    }
+  }
+};
+
 // src[0..63] (fp32, of which the first n >= 1 are valid; the rest read as
 // 0) straight into LDS dst[0..63], one value per lane; lane4 = 4 * lane,
 // pinned by the caller.
