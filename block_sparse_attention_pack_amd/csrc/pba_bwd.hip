@@ -93,44 +93,39 @@ __device__ __forceinline__ void dq_tile(f32x16 (&dq)[D / 32], const bf16x8 (&qop
 template <int D, int WGH>
 __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(1024))) bf16 sK[2][64 * C::STR];
-  __shared__ __attribute__((aligned(1024))) bf16 sV[2][64 * C::STR];
+  constexpr int T = 64 * C::STR;  // elements of one K or V tile
+  // K/V double buffers K(0) V(0) K(1) V(1); the dQ block leaves through LDS.
+  __shared__ __attribute__((aligned(1024))) bf16 lds[4 * T];
+  constexpr int R = 32 * (4 / WGH);  // query rows of the workgroup
+  using Blk = RowBlock<R, WGH * D * 2>;
+  static_assert(R * Blk::LSTR <= 4 * T * 2, "dQ block fits the LDS buffers");
+  auto sK = [&](int buf) { return lds + (2 * buf) * T; };
+  auto sV = [&](int buf) { return lds + (2 * buf + 1) * T; };
 
   const MapView& mp = a.qmap;
-  if (cptr(mp.status)[0] != 0) return;
+  // The status and the work-order entry are read together (one memory
+  // round trip); nothing is used before the status check.
+  const int map_status = cptr(mp.status)[0];
+  const int order_entry = cptr(mp.q_order)[blockIdx.x / (a.Hq / WGH)];
+  // (Using the values and the list pointers here keeps the compiler from
+  // sinking these loads, and the argument loads they need, below the branch:
+  // each would cost a memory round trip before the first tile's loads.)
+  asm volatile("" ::"s"(map_status), "s"(order_entry), "s"(mp.q2k_cnt), "s"(mp.q2k_idx));
+  if (map_status != 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int nhg = a.Hq / WGH;
-  const int item = cptr(mp.q_order)[blockIdx.x / nhg];
+  const int item = min(max(order_entry, 0), mp.B * mp.nqt - 1);
   const int b = item / mp.nqt, qt = item % mp.nqt;
-  const int h = (blockIdx.x % nhg) * WGH + (w % WGH);
+  const int h0 = (blockIdx.x % nhg) * WGH;
+  const int hw = w % WGH, qb = w / WGH;  // this wave's head and 32-query block
+  const int h = h0 + hw;
   const int g = h / a.G;
   const int S = a.S, Hq = a.Hq, Hkv = a.Hkv;
-  const int qi = qt * (32 * (4 / WGH)) + (w / WGH) * 32 + l32;
+  const int q0 = qt * R;
+  const int qi = q0 + qb * 32 + l32;
   const int qc = min(qi, S - 1);
-
-  // Q^T and dO^T as B operands; Delta = rowsum(dO * O) from the same lanes.
-  bf16x8 qop[C::NS], dop[C::NS];
-  float delta = 0.f;
-  {
-    const int64_t off = (((int64_t)b * S + qc) * Hq + h) * D + 8 * hi;
-#pragma unroll
-    for (int st = 0; st < C::NS; ++st) {
-      qop[st] = *(const bf16x8*)(a.q + off + 16 * st);
-      dop[st] = *(const bf16x8*)(a.dout + off + 16 * st);
-      const bf16x8 ov = *(const bf16x8*)(a.o + off + 16 * st);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) delta += (float)dop[st][t] * (float)ov[t];
-    }
-    delta += wave_half_swap(delta);
-  }
-  const int4 wv = reinterpret_cast<const int4*>(mp.tok_win)[(int64_t)b * S + qc];
-  const int wlo = qi < S ? wv.x : qi + 1, wplo = qi < S ? wv.y : 0, wphi = qi < S ? wv.z : 0;
-  const float lse = a.lse[((int64_t)b * Hq + h) * S + qc];
-  // log2-domain LSE; a row that sees no key (LSE = -inf) is masked on every
-  // tile it meets, and 0 keeps its arithmetic finite.
-  const float l2 = lse == kNegInf ? 0.f : lse * kLog2e;
 
   const int64_t lrow = (int64_t)b * mp.nqt + qt;
   const cint_ptr cnt = cptr(mp.q2k_cnt) + lrow * 2;
@@ -143,15 +138,44 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   const bf16* vb = a.v + ((int64_t)b * S * Hkv + g) * D;
   const Stager<D, C::STR> kst(tid, kvstride);  // K and V tiles have the same shape
 
+  // The first K/V tile's loads are issued before the Q / dO / O loads and
+  // the Delta arithmetic that waits for them, so that both latencies overlap.
+  const int first = list[0];  // valid memory even for an empty list
+  asm volatile("" ::"s"(first), "s"(n));
+  if (n > 0) {
+    const int k0 = min(max(first, 0), mp.nkt - 1) * 64;
+    kst.stage(sK(0), kb + (int64_t)k0 * kvstride, S - k0);
+    kst.stage(sV(0), vb + (int64_t)k0 * kvstride, S - k0);
+  }
+
+  // Q^T and dO^T as B operands; Delta = rowsum(dO * O) from the same lanes.
+  bf16x8 qop[C::NS], dop[C::NS], oop[C::NS];
+  {
+    const int64_t off = (((int64_t)b * S + qc) * Hq + h) * D + 8 * hi;
+#pragma unroll
+    for (int st = 0; st < C::NS; ++st) {
+      qop[st] = *(const bf16x8*)(a.q + off + 16 * st);
+      dop[st] = *(const bf16x8*)(a.dout + off + 16 * st);
+      oop[st] = *(const bf16x8*)(a.o + off + 16 * st);
+    }
+  }
+  const int4 wv = reinterpret_cast<const int4*>(mp.tok_win)[(int64_t)b * S + qc];
+  const float lse = a.lse[((int64_t)b * Hq + h) * S + qc];
+  float delta = 0.f;
+#pragma unroll
+  for (int st = 0; st < C::NS; ++st)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) delta += (float)dop[st][t] * (float)oop[st][t];
+  delta += wave_half_swap(delta);
+  const int wlo = qi < S ? wv.x : qi + 1, wplo = qi < S ? wv.y : 0, wphi = qi < S ? wv.z : 0;
+  // log2-domain LSE; a row that sees no key (LSE = -inf) is masked on every
+  // tile it meets, and 0 keeps its arithmetic finite.
+  const float l2 = lse == kNegInf ? 0.f : lse * kLog2e;
+
   f32x16 dq[C::NE];
 #pragma unroll
   for (int e = 0; e < C::NE; ++e) dq[e] = f32x16{};
 
-  if (n > 0) {
-    const int k0 = min(max(list[0], 0), mp.nkt - 1) * 64;
-    kst.stage(sK[0], kb + (int64_t)k0 * kvstride, S - k0);
-    kst.stage(sV[0], vb + (int64_t)k0 * kvstride, S - k0);
-  }
   wait_vmem();
   __syncthreads();
   // One visit: the next tile's loads go into the other buffer, then this
@@ -163,15 +187,15 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
     const int buf = j & 1;
     if (j + 1 < n) {
       const int k0 = min(max(list[j + 1], 0), mp.nkt - 1) * 64;
-      kst.stage(sK[buf ^ 1], kb + (int64_t)k0 * kvstride, S - k0);
-      kst.stage(sV[buf ^ 1], vb + (int64_t)k0 * kvstride, S - k0);
+      kst.stage(sK(buf ^ 1), kb + (int64_t)k0 * kvstride, S - k0);
+      kst.stage(sV(buf ^ 1), vb + (int64_t)k0 * kvstride, S - k0);
     }
     if constexpr (decltype(masked)::value) {
       const int jb = kt * 64 + 4 * hi;
-      dq_tile<D, true>(dq, qop, dop, l2, delta, sK[buf], sV[buf], a.scale_log2, qi - jb, wlo - jb, jb - wplo,
+      dq_tile<D, true>(dq, qop, dop, l2, delta, sK(buf), sV(buf), a.scale_log2, qi - jb, wlo - jb, jb - wplo,
                        wphi - wplo, lane);
     } else {
-      dq_tile<D, false>(dq, qop, dop, l2, delta, sK[buf], sV[buf], a.scale_log2, 0, 0, 0, 0, lane);
+      dq_tile<D, false>(dq, qop, dop, l2, delta, sK(buf), sV(buf), a.scale_log2, 0, 0, 0, 0, lane);
     }
     wait_vmem();
     __syncthreads();
@@ -186,8 +210,10 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
     a.delta[((int64_t)b * Hq + h) * S + qi] = delta;
     a.lse2[((int64_t)b * Hq + h) * S + qi] = l2;
   }
-  if (qi < S) {
-    bf16* row = a.dq + (((int64_t)b * S + qi) * Hq + h) * D + 4 * hi;
+  // dQ (bf16, times the softmax scale) through LDS, free after the last
+  // barrier, so that its rows leave as whole contiguous segments.
+  {
+    char* row = (char*)lds + (qb * 32 + l32) * Blk::LSTR + hw * D * 2 + 8 * hi;
 #pragma unroll
     for (int e = 0; e < C::NE; ++e) {
 #pragma unroll
@@ -195,10 +221,13 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
         bf16x4 v;
 #pragma unroll
         for (int t = 0; t < 4; ++t) v[t] = (bf16)(dq[e][4 * rg + t] * a.scale);
-        *(bf16x4*)(row + 32 * e + 8 * rg) = v;
+        *(bf16x4*)(row + 2 * (32 * e + 8 * rg)) = v;
       }
     }
   }
+  __syncthreads();
+  Blk::template store<256>(a.dq + ((int64_t)b * S + q0) * Hq * D + (int64_t)h0 * D, (const char*)lds, min(R, S - q0),
+                           Hq * D * 2, tid);
 }
 
 // ---------------------------------------------------------------------------

@@ -125,13 +125,21 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   static_assert(Blk::BYTES <= 2 * T * 2 && R * Blk::LSTR <= 4 * T * 2, "Q / O block fits the LDS buffers");
 
   const MapView& mp = a.map;
-  if (cptr(mp.status)[0] != 0) return;
+  // The status and the work-order entry are read together (one memory
+  // round trip); nothing is used before the status check.
+  const int map_status = cptr(mp.status)[0];
+  const int order_entry = cptr(mp.q_order)[blockIdx.x / (a.Hq / WGH)];
+  // (Using the values and the list pointers here keeps the compiler from
+  // sinking these loads, and the argument loads they need, below the branch:
+  // each would cost a memory round trip before the first tile's loads.)
+  asm volatile("" ::"s"(map_status), "s"(order_entry), "s"(mp.q2k_cnt), "s"(mp.q2k_idx));
+  if (map_status != 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
   const int l32 = lane & 31, hi = lane >> 5;
   const int nhg = a.Hq / WGH;
   // b * nqt + qt, longest lists first (clamped like every map read below)
-  const int item = min(max(cptr(mp.q_order)[blockIdx.x / nhg], 0), mp.B * mp.nqt - 1);
+  const int item = min(max(order_entry, 0), mp.B * mp.nqt - 1);
   const int b = item / mp.nqt, qt = item % mp.nqt;
   const int h0 = (blockIdx.x % nhg) * WGH;
   const int hw = w % WGH, qb = w / WGH;  // this wave's head and 32-query block
@@ -162,8 +170,10 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
 
   // Prologue: the Q block and the first K/V tile, all as direct loads.
   Blk::template load<4>(q_lds, a.q + ((int64_t)b * S + q0) * Hq * D + (int64_t)h0 * D, qrows, qrow_bytes, w, lane);
+  const int first = list[0];  // valid memory even for an empty list
+  asm volatile("" ::"s"(first), "s"(n));
   if (n > 0) {
-    const int k0 = min(max(list[0], 0), mp.nkt - 1) * 64;
+    const int k0 = min(max(first, 0), mp.nkt - 1) * 64;
     kst.stage(sK(0), kb + (int64_t)k0 * kvstride, S - k0);
     kst.stage(sV(0), vb + (int64_t)k0 * kvstride, S - k0);
   }
