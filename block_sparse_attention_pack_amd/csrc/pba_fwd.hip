@@ -34,6 +34,29 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 
+// Running-max update with a lazy reference (log2 domain): the reference m
+// moves only when the tile max exceeds it by more than kLazy, so most
+// tiles leave the accumulators as they are (alpha = 1).  Unnormalised
+// probabilities then stay below 2^kLazy, far inside the range of the fp32
+// accumulators and of bf16.  The result does not depend on the reference
+// (O and LSE are normalised by the same running sum), up to rounding.
+constexpr float kLazy = 8.f;
+__device__ __forceinline__ float lazy_reference(float& m, float mx, float& alpha) {
+  const bool move = mx > m + kLazy;  // any finite mx moves m = -inf
+  alpha = move ? fast_exp2(m - mx) : 1.f;
+  m = move ? mx : m;
+  return m == kNegInf ? 0.f : m;
+}
+
+// O^T *= alpha, skipped when every lane's alpha is 1 (wave-uniform branch).
+template <int D>
+__device__ __forceinline__ void rescale(f32x16 (&o)[D / 32], float alpha) {
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+    for (int e = 0; e < D / 32; ++e) o[e] *= alpha;
+  }
+}
+
 template <int D>
 struct FwdCfg {
   static constexpr int NS = D / 16;  // MFMA k-steps over the head dim
@@ -42,18 +65,20 @@ struct FwdCfg {
   static constexpr int VSTR = D + 8;   // V tile row stride (elements)
 };
 
-// One key tile for one wave: S^T = K Q^T (64 keys x 32 queries), online
-// softmax (masked on partial tiles), O^T = alpha O^T + V^T P^T.
-// Key j = k0 + 32*aa + 8*(r/4) + 4*hi + r%4 sits in register r of s[aa];
-// with jb = k0 + 4*hi and o the compile-time part, j is visible to the
-// lane's query iff o <= lim and (o >= lo or (unsigned)(o + pc) < plen).
-template <int D, bool MASK>
-__device__ __forceinline__ void fwd_tile(f32x16 (&o)[D / 32], float& m, float& l, const bf16x8 (&qop)[D / 16],
-                                         const bf16* __restrict__ sk, const bf16* __restrict__ sv, float scale_log2,
-                                         int lim, int lo, int pc, int plen, int lane) {
+// The three parts of a key tile for one wave (64 keys x 32 queries).  The
+// kernel runs them software-pipelined: in one step, the scores of tile j+1,
+// the softmax of tile j and the P V product of tile j-1 are independent, so
+// MFMAs of one part overlap the vector ALU work of another within the wave.
+
+// S^T = K Q^T.  Key k0 + 32*aa + 8*(r/4) + 4*hi + r%4 sits in register r of
+// s[aa]; the lane's query column is lane % 32.
+template <int D>
+__device__ __forceinline__ void fwd_scores(f32x16 (&s)[2], const bf16x8 (&qop)[D / 16], const bf16* __restrict__ sk,
+                                           int lane) {
   using C = FwdCfg<D>;
   const int l32 = lane & 31, hi = lane >> 5;
-  f32x16 s[2] = {f32x16{}, f32x16{}};
+  s[0] = f32x16{};
+  s[1] = f32x16{};
 #pragma unroll
   for (int st = 0; st < C::NS; ++st) {
 #pragma unroll
@@ -62,7 +87,16 @@ __device__ __forceinline__ void fwd_tile(f32x16 (&o)[D / 32], float& m, float& l
       s[aa] = mfma32(kop, qop[st], s[aa]);
     }
   }
-  sched_fence();
+}
+
+// Online softmax of one tile (masked on partial tiles): updates the running
+// reference m (log2 domain) and sum l, returns the rescale factor alpha of the
+// accumulators and P^T packed as bf16 B operands.  With jb = k0 + 4*hi and
+// o the compile-time part of a key's offset, the key is visible to the
+// lane's query iff o <= lim and (o >= lo or (unsigned)(o + pc) < plen).
+template <bool MASK>
+__device__ __forceinline__ void fwd_softmax(f32x16 (&s)[2], float& m, float& l, float& alpha, bf16x8 (&p)[2][2],
+                                            float scale_log2, int lim, int lo, int pc, int plen) {
   float mx = kNegInf;
 #pragma unroll
   for (int aa = 0; aa < 2; ++aa) {
@@ -77,12 +111,8 @@ __device__ __forceinline__ void fwd_tile(f32x16 (&o)[D / 32], float& m, float& l
     }
   }
   mx = fmaxf(mx, wave_half_swap(mx)) * scale_log2;
-  const float mnew = fmaxf(m, mx);
-  const float mref = mnew == kNegInf ? 0.f : mnew;
-  const float alpha = fast_exp2(m - mref);
-  m = mnew;
+  const float mref = lazy_reference(m, mx, alpha);
   float lsum = 0.f;
-  bf16x8 p[2][2];
 #pragma unroll
   for (int aa = 0; aa < 2; ++aa) {
 #pragma unroll
@@ -95,9 +125,92 @@ __device__ __forceinline__ void fwd_tile(f32x16 (&o)[D / 32], float& m, float& l
     p[aa][1] = pack8(s[aa], 8);
   }
   l = l * alpha + lsum;
-#pragma unroll
-  for (int e = 0; e < C::NE; ++e) o[e] *= alpha;
+}
+
+// One full pipeline step for one wave, hand-scheduled: the MFMAs of P V
+// for the previous tile (after the rescale by its alpha) and of the scores
+// for the next tile, each followed by a slice of the current tile's softmax
+// (mask and max while P V runs, exp and sum while the scores run), with
+// every MFMA's LDS operand read two MFMAs ahead.  On return s holds the
+// next tile's scores and p / alpha the current tile's P and rescale.
+template <int D, bool MASK>
+__device__ __forceinline__ void fwd_step(f32x16 (&o)[D / 32], bf16x8 (&p)[2][2], float& alpha, float& m, float& l,
+                                         f32x16 (&s)[2], const bf16x8 (&qop)[D / 16], const bf16* __restrict__ sk,
+                                         const bf16* __restrict__ sv, float scale_log2, int lim, int lo, int pc,
+                                         int plen, int lane) {
+  using C = FwdCfg<D>;
+  constexpr int NPV = C::NE * 4, NQK = C::NS * 2, N = NPV + NQK;
+  constexpr int NEXP = NQK - 2;  // score slices of the exp phase (the max arrives after two MFMAs)
+  const int l32 = lane & 31, hi = lane >> 5;
+  auto operand = [&](int i) -> bf16x8 {
+    if (i < NPV) {
+      const int e = i >> 2, aa = (i >> 1) & 1, u = i & 1;
+      const int r0 = 32 * aa + 16 * u + 4 * hi;
+      return lds_tr8p(sv, C::VSTR, r0, r0 + 8, 32 * e, lane);
+    }
+    const int k = i - NPV, st = k >> 1, aa = k & 1;
+    return *(const bf16x8*)(sk + prow(32 * aa + l32) * C::KSTR + 16 * st + 8 * hi);
+  };
+  rescale<D>(o, alpha);
+  bf16x8 ops[3];
+  ops[0] = operand(0);
+  ops[1] = operand(1);
+  f32x16 sn[2] = {f32x16{}, f32x16{}};
+  float mx = kNegInf, mref = 0.f, lsum = 0.f;
   sched_fence();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + 2 < N) ops[(i + 2) % 3] = operand(i + 2);
+    if (i < NPV) {
+      const int e = i >> 2, aa = (i >> 1) & 1, u = i & 1;
+      o[e] = mfma32(ops[i % 3], p[aa][u], o[e]);
+      // Mask and max of scores [32 i / NPV, 32 (i + 1) / NPV).
+#pragma unroll
+      for (int x = 32 * i / NPV; x < 32 * (i + 1) / NPV; ++x) {
+        const int sa = x >> 4, r = x & 15;
+        if (MASK) {
+          const int off = 32 * sa + 8 * (r >> 2) + (r & 3);
+          // (bitwise, not short-circuit: no branches between the MFMAs)
+          const bool ok = (off <= lim) & ((off >= lo) | ((unsigned)(off + pc) < (unsigned)plen));
+          s[sa][r] = ok ? s[sa][r] : kNegInf;
+        }
+        mx = fmaxf(mx, s[sa][r]);
+      }
+    } else {
+      const int k = i - NPV, st = k >> 1, aa = k & 1;
+      sn[aa] = mfma32(ops[i % 3], qop[st], sn[aa]);
+      if (k == 1) {
+        mref = lazy_reference(m, half_max(mx) * scale_log2, alpha);
+      }
+      if (k >= 2) {
+        const int c = k - 2;
+#pragma unroll
+        for (int x = 32 * c / NEXP; x < 32 * (c + 1) / NEXP; ++x) {
+          const int sa = x >> 4, r = x & 15;
+          const float ev = fast_exp2(__builtin_fmaf(s[sa][r], scale_log2, -mref));
+          s[sa][r] = ev;
+          lsum += ev;
+        }
+      }
+    }
+    sched_fence();
+  }
+  p[0][0] = pack8(s[0], 0);
+  p[0][1] = pack8(s[0], 8);
+  p[1][0] = pack8(s[1], 0);
+  p[1][1] = pack8(s[1], 8);
+  l = l * alpha + lsum;
+  s[0] = sn[0];
+  s[1] = sn[1];
+}
+
+// O^T = alpha O^T + V^T P^T, V^T read with LDS transpose reads.
+template <int D>
+__device__ __forceinline__ void fwd_pv(f32x16 (&o)[D / 32], const bf16x8 (&p)[2][2], float alpha,
+                                       const bf16* __restrict__ sv, int lane) {
+  using C = FwdCfg<D>;
+  const int hi = lane >> 5;
+  rescale<D>(o, alpha);
 #pragma unroll
   for (int e = 0; e < C::NE; ++e) {
 #pragma unroll
@@ -117,8 +230,8 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   static_assert(C::KSTR == C::VSTR, "K and V tiles share one stager");
   constexpr int T = 64 * C::KSTR;  // elements of one K or V tile
-  // K/V double buffers: K(0) V(0) K(1) V(1).  The workgroup's Q block is
-  // first staged in the second pair and its O block leaves through LDS.
+  // K(0) K(1) V(0) V(1) double buffers.  The workgroup's Q block is first
+  // staged in the V pair and its O block leaves through LDS.
   __shared__ __attribute__((aligned(1024))) bf16 lds[4 * T];
   constexpr int R = 32 * (4 / WGH);  // query rows of the workgroup
   using Blk = RowBlock<R, WGH * D * 2>;
@@ -150,8 +263,8 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   const int qi = q0 + qb * 32 + l32;  // this lane's query
   const int qrows = min(R, S - q0);
   const int qrow_bytes = Hq * D * 2;
-  char* const qo_lds = (char*)lds;  // the Q block (second buffer pair) and later the O block
-  char* const q_lds = qo_lds + 2 * T * 2;
+  char* const qo_lds = (char*)lds;  // the O block at the end
+  char* const q_lds = qo_lds + 2 * T * 2;  // the Q block at the start (the V pair)
 
   const int64_t lrow = (int64_t)b * mp.nqt + qt;
   // Counts are clamped so that even a corrupted map cannot index outside
@@ -165,18 +278,19 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   const bf16* kb = a.k + ((int64_t)b * S * Hkv + g) * D;
   const bf16* vb = a.v + ((int64_t)b * S * Hkv + g) * D;
   const Stager<D, C::KSTR> kst(tid, kvstride);
-  auto sK = [&](int buf) { return lds + (2 * buf) * T; };
-  auto sV = [&](int buf) { return lds + (2 * buf + 1) * T; };
+  auto sK = [&](int t) { return lds + (t & 1) * T; };        // K of visit t
+  auto sV = [&](int t) { return lds + (2 + (t & 1)) * T; };  // V of visit t
+  auto key0 = [&](int t) { return min(max(list[t], 0), mp.nkt - 1) * 64; };
 
-  // Prologue: the Q block and the first K/V tile, all as direct loads.
+  // Prologue: the Q block and the first two K tiles, all as direct loads.
   Blk::template load<4>(q_lds, a.q + ((int64_t)b * S + q0) * Hq * D + (int64_t)h0 * D, qrows, qrow_bytes, w, lane);
   const int first = list[0];  // valid memory even for an empty list
   asm volatile("" ::"s"(first), "s"(n));
   if (n > 0) {
     const int k0 = min(max(first, 0), mp.nkt - 1) * 64;
     kst.stage(sK(0), kb + (int64_t)k0 * kvstride, S - k0);
-    kst.stage(sV(0), vb + (int64_t)k0 * kvstride, S - k0);
   }
+  if (n > 1) kst.stage(sK(1), kb + (int64_t)key0(1) * kvstride, S - key0(1));
   int wlo, wplo, wphi;
   {
     const int4 wv = reinterpret_cast<const int4*>(mp.tok_win)[(int64_t)b * S + min(qi, S - 1)];
@@ -193,42 +307,75 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int st = 0; st < C::NS; ++st) qop[st] = *(const bf16x8*)(qr + 32 * st);
   }
-  __syncthreads();  // the second buffer pair is free again
 
-  float m = kNegInf, l = 0.f;
+  float m = kNegInf, l = 0.f, alpha = 1.f;
   f32x16 o[C::NE];
 #pragma unroll
   for (int e = 0; e < C::NE; ++e) o[e] = f32x16{};
+  f32x16 s[2];
+  bf16x8 p[2][2];
+  if (n > 0) fwd_scores<D>(s, qop, sK(0), lane);
+  __syncthreads();  // the Q block and K(0) have been read by every wave
 
-  // One visit: start the next tile's loads into the other buffer (last read
-  // in the previous visit, which every wave has left), then this tile's math.
-  auto visit = [&](int j, auto masked) {
-    const int kt = min(max(list[j], 0), mp.nkt - 1);
-    const int buf = j & 1;
-    if (j + 1 < n) {
-      const int k0 = min(max(list[j + 1], 0), mp.nkt - 1) * 64;
-      kst.stage(sK(buf ^ 1), kb + (int64_t)k0 * kvstride, S - k0);
-      kst.stage(sV(buf ^ 1), vb + (int64_t)k0 * kvstride, S - k0);
-    }
-    if constexpr (decltype(masked)::value) {
-      const int jb = kt * 64 + 4 * hi;
-      fwd_tile<D, true>(o, m, l, qop, sK(buf), sV(buf), a.scale_log2, qi - jb, wlo - jb, jb - wplo, wphi - wplo, lane);
+  // Step j (software pipeline): loads of V(j) and K(j+2) go into buffers
+  // last read in step j-1; then P V of tile j-1, the scores of tile j+1
+  // (K(j+1) was loaded in step j-1) and the softmax of tile j, which are
+  // independent of one another.  One barrier per step.
+  auto step = [&](int j, auto masked, auto has_prev, auto has_next) {
+    kst.stage(sV(j), vb + (int64_t)key0(j) * kvstride, S - key0(j));
+    if (j + 2 < n) kst.stage(sK(j), kb + (int64_t)key0(j + 2) * kvstride, S - key0(j + 2));
+    const int jb = key0(j) + 4 * hi;
+    constexpr bool MASKED = decltype(masked)::value;
+    if constexpr (decltype(has_prev)::value && decltype(has_next)::value) {
+      if constexpr (MASKED)
+        fwd_step<D, true>(o, p, alpha, m, l, s, qop, sK(j + 1), sV(j - 1), a.scale_log2, qi - jb, wlo - jb,
+                          jb - wplo, wphi - wplo, lane);
+      else
+        fwd_step<D, false>(o, p, alpha, m, l, s, qop, sK(j + 1), sV(j - 1), a.scale_log2, 0, 0, 0, 0, lane);
     } else {
-      fwd_tile<D, false>(o, m, l, qop, sK(buf), sV(buf), a.scale_log2, 0, 0, 0, 0, lane);
+      if constexpr (decltype(has_prev)::value) fwd_pv<D>(o, p, alpha, sV(j - 1), lane);
+      f32x16 sn[2];
+      if constexpr (decltype(has_next)::value) fwd_scores<D>(sn, qop, sK(j + 1), lane);
+      if constexpr (MASKED)
+        fwd_softmax<true>(s, m, l, alpha, p, a.scale_log2, qi - jb, wlo - jb, jb - wplo, wphi - wplo);
+      else
+        fwd_softmax<false>(s, m, l, alpha, p, a.scale_log2, 0, 0, 0, 0);
+      if constexpr (decltype(has_next)::value) {
+        s[0] = sn[0];
+        s[1] = sn[1];
+      }
     }
+    // The softmax results are complete here: without this the compiler may
+    // sink the softmax below the barrier.
+    asm volatile("" ::"v"(p[0][0]), "v"(p[0][1]), "v"(p[1][0]), "v"(p[1][1]), "v"(alpha), "v"(l));
     wait_vmem();
     __syncthreads();
   };
-  // Full tiles come first in the list, then partial ones.  Two loops rather
-  // than a branch in one keep each loop's accumulators in place (a merge of
-  // two paths inside one loop body costs a copy of every accumulator).
-  int j = 0;
-  for (; j < nfull; ++j) visit(j, std::false_type{});
-  for (; j < n; ++j) visit(j, std::true_type{});
+  using F = std::false_type;
+  using Tr = std::true_type;
+  // Full tiles come first in the list, then partial ones.  The first and the
+  // last step are peeled, and the steps between run in two loops (full,
+  // partial) rather than one loop with a branch, which would make the
+  // compiler copy every accumulator at the merge.
+  if (n > 0) {
+    if (n > 1) {
+      if (nfull > 0) step(0, F{}, F{}, Tr{});
+      else step(0, Tr{}, F{}, Tr{});
+      int j = 1;
+      for (; j < min(nfull, n - 1); ++j) step(j, F{}, Tr{}, Tr{});
+      for (; j < n - 1; ++j) step(j, Tr{}, Tr{}, Tr{});
+      if (n - 1 < nfull) step(n - 1, F{}, Tr{}, F{});
+      else step(n - 1, Tr{}, Tr{}, F{});
+    } else {
+      if (nfull > 0) step(0, F{}, F{}, F{});
+      else step(0, Tr{}, F{}, F{});
+    }
+    fwd_pv<D>(o, p, alpha, sV(n - 1), lane);
+    __syncthreads();  // every wave is done with V(n-1) before O goes to LDS
+  }
 
-  // Epilogue: normalise; O (bf16) goes through LDS (free after the last
-  // barrier) so that its rows leave as whole contiguous segments; LSE in
-  // natural log.
+  // Epilogue: normalise; O (bf16) goes through LDS so that its rows leave
+  // as whole contiguous segments; LSE in natural log.
   const float lt = l + wave_half_swap(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   {

@@ -256,6 +256,16 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float wave_half_swap(float x) { return __shfl_xor(x, 32); }
 
+// max(x of this lane, x of lane ^ 32) with one VALU permute (no LDS trip):
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second, so afterwards {a, b} hold both halves' values
+// in every lane.
+__device__ __forceinline__ float half_max(float x) {
+  float a = x, b = x;
+  asm volatile("v_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
