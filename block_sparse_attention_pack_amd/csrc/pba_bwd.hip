@@ -42,63 +42,95 @@ struct BwdCfg {
 // bwd_dq
 // ---------------------------------------------------------------------------
 
-// One key tile for one wave of bwd_dq (64 keys x 32 queries).  Key
+// One key tile for one wave of bwd_dq (64 keys x 32 queries), hand-
+// scheduled.  Per 32-key half aa: S^T = K Q^T and dP^T = V dO^T (16 MFMAs),
+// dS^T = P^T (dP^T - Delta) with P^T = exp2(S^T * scale_log2 - LSE2)
+// (vector ALU), then dQ^T += K^T dS^T (8 MFMAs, K^T by transpose reads).
+// The halves are staggered so that the vector work of one half runs
+// between the MFMAs of the other: S/dP of half 0, S/dP of half 1 with the
+// dS of half 0, dQ of half 0 with the dS of half 1, dQ of half 1.  Every
+// MFMA's LDS operand is read two MFMAs ahead.  Key
 // j = k0 + 32*aa + 8*(r/4) + 4*hi + r%4 sits in register r of s[aa]; the
-// mask parameters are those of the forward (see fwd_tile).
+// mask parameters are those of the forward.
 template <int D, bool MASK>
 __device__ __forceinline__ void dq_tile(f32x16 (&dq)[D / 32], const bf16x8 (&qop)[D / 16],
                                         const bf16x8 (&dop)[D / 16], float l2, float delta,
                                         const bf16* __restrict__ sk, const bf16* __restrict__ sv, float scale_log2,
                                         int lim, int lo, int pc, int plen, int lane) {
   using C = BwdCfg<D>;
+  constexpr int NSD = 2 * C::NS;    // S and dP MFMAs of one half
+  constexpr int NDQ = 2 * C::NE;    // dQ MFMAs of one half
+  constexpr int N = 2 * NSD + 2 * NDQ;
   const int l32 = lane & 31, hi = lane >> 5;
-  // The two 32-key halves one after the other (fewer live registers).
+  auto operand = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+    if (i < 2 * NSD) {  // S (even) / dP (odd) of half i / NSD, k-step (i % NSD) / 2
+      const int aa = i / NSD, st = (i % NSD) >> 1;
+      const bf16* t = (i & 1) ? sv : sk;
+      return *(const bf16x8*)(t + prow(32 * aa + l32) * C::STR + 16 * st + 8 * hi);
+    }
+    const int k = i - 2 * NSD, aa = k / NDQ, e = (k % NDQ) >> 1, u = k & 1;
+    const int r0 = 32 * aa + 16 * u + 4 * hi;
+    return lds_tr8p(sk, C::STR, r0, r0 + 8, 32 * e, lane);
+  };
+  // dS of score x (0..15) of half aa, in place in s[aa].
+  auto dscore = [&](f32x16 (&sa)[2], f32x16 (&pa)[2], int aa, int r) __attribute__((always_inline)) {
+    float p = fast_exp2(__builtin_fmaf(sa[aa][r], scale_log2, -l2));
+    if (MASK) {
+      const int off = 32 * aa + 8 * (r >> 2) + (r & 3);
+      // (bitwise, not short-circuit: no branches between the MFMAs)
+      const bool ok = (off <= lim) & ((off >= lo) | ((unsigned)(off + pc) < (unsigned)plen));
+      p = ok ? p : 0.f;
+    }
+    sa[aa][r] = p * (pa[aa][r] - delta);
+  };
+  f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+  bf16x8 ds[2][2];
+  bf16x8 ops[3];
+  ops[0] = operand(0);
+  ops[1] = operand(1);
+  sched_fence();
+  static_for<0, N>([&](auto ic) __attribute__((always_inline)) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i + 2 < N) ops[(i + 2) % 3] = operand(i + 2);
+    if constexpr (i < 2 * NSD) {
+      constexpr int aa = i / NSD, st = (i % NSD) >> 1;
+      if constexpr (i & 1) dp[aa] = mfma32(ops[i % 3], dop[st], dp[aa]);
+      else s[aa] = mfma32(ops[i % 3], qop[st], s[aa]);
+      if constexpr (aa == 1) {  // dS of half 0, 16 scores over NSD slices
+        constexpr int c = i - NSD;
 #pragma unroll
-  for (int aa = 0; aa < 2; ++aa) {
-    f32x16 s = f32x16{}, dp = f32x16{};
+        for (int x = 16 * c / NSD; x < 16 * (c + 1) / NSD; ++x) dscore(s, dp, 0, x);
+        if constexpr (c == NSD - 1) {
+          ds[0][0] = pack8(s[0], 0);
+          ds[0][1] = pack8(s[0], 8);
+        }
+      }
+    } else {
+      constexpr int k = i - 2 * NSD, aa = k / NDQ, e = (k % NDQ) >> 1, u = k & 1;
+      dq[e] = mfma32(ops[i % 3], ds[aa][u], dq[e]);
+      if constexpr (aa == 0) {  // dS of half 1, 16 scores over NDQ slices
 #pragma unroll
-    for (int st = 0; st < C::NS; ++st) {
-      const bf16x8 kop = *(const bf16x8*)(sk + prow(32 * aa + l32) * C::STR + 16 * st + 8 * hi);
-      s = mfma32(kop, qop[st], s);
-      const bf16x8 vop = *(const bf16x8*)(sv + prow(32 * aa + l32) * C::STR + 16 * st + 8 * hi);
-      dp = mfma32(vop, dop[st], dp);
+        for (int x = 16 * k / NDQ; x < 16 * (k + 1) / NDQ; ++x) dscore(s, dp, 1, x);
+        if constexpr (k == NDQ - 1) {
+          ds[1][0] = pack8(s[1], 0);
+          ds[1][1] = pack8(s[1], 8);
+        }
+      }
     }
     sched_fence();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -l2));
-      if (MASK) {
-        const int off = 32 * aa + 8 * (r >> 2) + (r & 3);
-        const bool ok = off <= lim && (off >= lo || (unsigned)(off + pc) < (unsigned)plen);
-        p = ok ? p : 0.f;
-      }
-      s[r] = p * (dp[r] - delta);
-    }
-    const bf16x8 ds[2] = {pack8(s, 0), pack8(s, 8)};
-    sched_fence();
-    // dQ^T += K^T dS^T: A = K^T by transpose reads, B = dS^T (key order of
-    // the accumulator layout).
-#pragma unroll
-    for (int e = 0; e < C::NE; ++e) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int r0 = 32 * aa + 16 * u + 4 * hi;
-        const bf16x8 kt = lds_tr8p(sk, C::STR, r0, r0 + 8, 32 * e, lane);
-        dq[e] = mfma32(kt, ds[u], dq[e]);
-      }
-    }
-  }
+  });
 }
 
 template <int D, int WGH>
 __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   using C = BwdCfg<D>;
   constexpr int T = 64 * C::STR;  // elements of one K or V tile
-  // K/V double buffers K(0) V(0) K(1) V(1); the dQ block leaves through LDS.
+  // K/V double buffers K(0) V(0) K(1) V(1).  The Q, dO and O blocks come
+  // in through the pairs and the dQ block leaves through LDS.
   __shared__ __attribute__((aligned(1024))) bf16 lds[4 * T];
   constexpr int R = 32 * (4 / WGH);  // query rows of the workgroup
   using Blk = RowBlock<R, WGH * D * 2>;
-  static_assert(R * Blk::LSTR <= 4 * T * 2, "dQ block fits the LDS buffers");
+  static_assert(Blk::BYTES <= 2 * T * 2, "a Q / dO / O block fits one buffer pair");
   auto sK = [&](int buf) { return lds + (2 * buf) * T; };
   auto sV = [&](int buf) { return lds + (2 * buf + 1) * T; };
 
@@ -138,34 +170,45 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   const bf16* vb = a.v + ((int64_t)b * S * Hkv + g) * D;
   const Stager<D, C::STR> kst(tid, kvstride);  // K and V tiles have the same shape
 
-  // The first K/V tile's loads are issued before the Q / dO / O loads and
-  // the Delta arithmetic that waits for them, so that both latencies overlap.
+  // Prologue in two rounds of direct (whole-row) loads, as the three row
+  // blocks and the first K/V tile do not fit in LDS at once: Q and dO into
+  // the two buffer pairs, then O and the first K/V tile.
+  char* const pair0 = (char*)lds;             // K(0) V(0)
+  char* const pair1 = (char*)(lds + 2 * T);   // K(1) V(1)
+  const int qrows = min(R, S - q0), qrow_bytes = Hq * D * 2;
+  const int64_t blk = ((int64_t)b * S + q0) * Hq * D + (int64_t)h0 * D;
+  Blk::template load<4>(pair1, a.q + blk, qrows, qrow_bytes, w, lane);
+  Blk::template load<4>(pair0, a.dout + blk, qrows, qrow_bytes, w, lane);
   const int first = list[0];  // valid memory even for an empty list
-  asm volatile("" ::"s"(first), "s"(n));
+  const int4 wv = reinterpret_cast<const int4*>(mp.tok_win)[(int64_t)b * S + qc];
+  const float lse = a.lse[((int64_t)b * Hq + h) * S + qc];
+  wait_vmem();
+  __syncthreads();
+  // Q^T and dO^T as B operands: lane holds query qi, head dims 16*st + 8*hi + 0..7.
+  bf16x8 qop[C::NS], dop[C::NS];
+  const int rofs = (qb * 32 + l32) * Blk::LSTR + hw * D * 2 + 16 * hi;
+#pragma unroll
+  for (int st = 0; st < C::NS; ++st) {
+    qop[st] = *(const bf16x8*)(pair1 + rofs + 32 * st);
+    dop[st] = *(const bf16x8*)(pair0 + rofs + 32 * st);
+  }
+  __syncthreads();
   if (n > 0) {
     const int k0 = min(max(first, 0), mp.nkt - 1) * 64;
     kst.stage(sK(0), kb + (int64_t)k0 * kvstride, S - k0);
     kst.stage(sV(0), vb + (int64_t)k0 * kvstride, S - k0);
   }
-
-  // Q^T and dO^T as B operands; Delta = rowsum(dO * O) from the same lanes.
-  bf16x8 qop[C::NS], dop[C::NS], oop[C::NS];
-  {
-    const int64_t off = (((int64_t)b * S + qc) * Hq + h) * D + 8 * hi;
-#pragma unroll
-    for (int st = 0; st < C::NS; ++st) {
-      qop[st] = *(const bf16x8*)(a.q + off + 16 * st);
-      dop[st] = *(const bf16x8*)(a.dout + off + 16 * st);
-      oop[st] = *(const bf16x8*)(a.o + off + 16 * st);
-    }
-  }
-  const int4 wv = reinterpret_cast<const int4*>(mp.tok_win)[(int64_t)b * S + qc];
-  const float lse = a.lse[((int64_t)b * Hq + h) * S + qc];
+  Blk::template load<4>(pair1, a.o + blk, qrows, qrow_bytes, w, lane);
+  wait_vmem();
+  __syncthreads();
+  // Delta = rowsum(dO * O) from the same lanes.
   float delta = 0.f;
 #pragma unroll
-  for (int st = 0; st < C::NS; ++st)
+  for (int st = 0; st < C::NS; ++st) {
+    const bf16x8 ov = *(const bf16x8*)(pair1 + rofs + 32 * st);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) delta += (float)dop[st][t] * (float)oop[st][t];
+    for (int t = 0; t < 8; ++t) delta += (float)dop[st][t] * (float)ov[t];
+  }
   delta += wave_half_swap(delta);
   const int wlo = qi < S ? wv.x : qi + 1, wplo = qi < S ? wv.y : 0, wphi = qi < S ? wv.z : 0;
   // log2-domain LSE; a row that sees no key (LSE = -inf) is masked on every
@@ -175,9 +218,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   f32x16 dq[C::NE];
 #pragma unroll
   for (int e = 0; e < C::NE; ++e) dq[e] = f32x16{};
-
-  wait_vmem();
-  __syncthreads();
+  __syncthreads();  // the O block has been read: the second pair is free
   // One visit: the next tile's loads go into the other buffer, then this
   // tile's math.  Full tiles precede partial ones in the list; a loop for
   // each keeps the dQ accumulators in place (two paths merging inside one

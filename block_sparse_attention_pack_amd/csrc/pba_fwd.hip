@@ -142,7 +142,7 @@ __device__ __forceinline__ void fwd_step(f32x16 (&o)[D / 32], bf16x8 (&p)[2][2],
   constexpr int NPV = C::NE * 4, NQK = C::NS * 2, N = NPV + NQK;
   constexpr int NEXP = NQK - 2;  // score slices of the exp phase (the max arrives after two MFMAs)
   const int l32 = lane & 31, hi = lane >> 5;
-  auto operand = [&](int i) -> bf16x8 {
+  auto operand = [&](int i) __attribute__((always_inline)) -> bf16x8 {
     if (i < NPV) {
       const int e = i >> 2, aa = (i >> 1) & 1, u = i & 1;
       const int r0 = 32 * aa + 16 * u + 4 * hi;

@@ -10,6 +10,8 @@
 //     M[r0 + s/4][c0 + 4*(s%4)] of a row-major matrix M, lane i receives
 //     M[r0 + t][c0 + i] for t = 0..3: a 4 x 16 block read column-wise.
 #pragma once
+#include <type_traits>
+
 #include "pba_internal.h"
 
 namespace pba {
@@ -119,6 +121,8 @@ struct Stager {
   static constexpr int NI = ROWS * STR * 2 / 1024;  // 1 KB instructions per tile
   static constexpr int PER_WAVE = (NI + NWAVES - 1) / NWAVES;
   static_assert((ROWS * STR * 2) % 1024 == 0, "tile must be whole 1 KB blocks");
+  // DMA instructions that wave w issues per stage() call.
+  static constexpr int issued(int w) { return NI - w * PER_WAVE < 0 ? 0 : (NI - w * PER_WAVE < PER_WAVE ? NI - w * PER_WAVE : PER_WAVE); }
   int off[PER_WAVE];  // byte offset of this lane's chunk from the tile's first row
   int w;
   int row_stride;
@@ -238,7 +242,37 @@ __device__ __forceinline__ void buffer_lds_dword(const float* src, int n, float*
 #endif
 }
 
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+// (hand-scheduled sequences index registers by I, which must be constant).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Waits until at most `keep` (wave-uniform, 0..15) vector memory
+// operations of this wave are outstanding: the older ones have completed,
+// the `keep` most recent may still be in flight (the counter retires in
+// issue order).  Other counters are not waited for.
+__device__ __forceinline__ void wait_vmem_keep(int keep) {
+#define PBA_WAIT_CASE(N) \
+  case N:                \
+    __builtin_amdgcn_s_waitcnt((N) | (7 << 4) | (15 << 8)); \
+    break;
+  switch (keep) {
+    PBA_WAIT_CASE(1) PBA_WAIT_CASE(2) PBA_WAIT_CASE(3) PBA_WAIT_CASE(4) PBA_WAIT_CASE(5) PBA_WAIT_CASE(6)
+    PBA_WAIT_CASE(7) PBA_WAIT_CASE(8) PBA_WAIT_CASE(9) PBA_WAIT_CASE(10) PBA_WAIT_CASE(11) PBA_WAIT_CASE(12)
+    PBA_WAIT_CASE(13) PBA_WAIT_CASE(14) PBA_WAIT_CASE(15)
+    default:
+      __builtin_amdgcn_s_waitcnt(0);
+      break;
+  }
+#undef PBA_WAIT_CASE
+}
 
 // Keeps the instruction scheduler from moving anything across this point
 // (used between the phases of a tile so that operand loads of a later
