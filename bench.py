@@ -150,6 +150,71 @@ def traffic_record(kernel):
     return rec
 
 
+def measured_mfma_peak(A, torch):
+    """Sustained bf16 MFMA rate of this device: the library's probe loop
+    (independent accumulators, every CU busy), in TFLOP/s."""
+    nb, iters = 2048, 200
+    out = torch.empty(nb * 256, dtype=torch.float32, device="cuda")
+    A.mfma_probe(out, nb, 10)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        A.mfma_probe(out, nb, iters)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, nb * iters * A.MFMA_PROBE_FLOP_PER_BLOCK_ITER / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return best
+
+
+def copy_bandwidth(torch):
+    """Device-to-device copy rate (read + write bytes per second), GB/s."""
+    src = torch.ones(1 << 27, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 5 * 2 * src.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return gbps
+
+
+def skip_cost(A, torch, steps, warmup, copy_gbps):
+    """The response-long workload (4 x 4352) and the same packs in rows
+    padded to 8448 tokens: skipped tiles should cost nothing beyond writing
+    the pad rows' zero outputs (predicted from the copy bandwidth)."""
+    from workloads.generate import make_workload, pad_to_len
+    w = make_workload(4, 0)
+    ps = w.packset
+    dev = torch.device("cuda:0")
+    att = lambda p: p["fwd"] + p["bwd_dq"] + p["bwd_dkdv"]  # noqa: E731
+    ts = {}
+    for S_new in (ps.S, 8448):
+        pps = pad_to_len(ps, S_new)
+        t = []
+        for x in (w.q, w.k, w.v, w.do):
+            y = torch.zeros((x.shape[0], S_new) + tuple(x.shape[2:]), dtype=x.dtype)
+            y[:, :ps.S] = x
+            t.append(y.to(dev).contiguous())
+        r = Runner(A, torch, pps, *t, w.Hq, w.Hkv, w.D, w.scale)
+        _, per = time_runner(torch, r, steps, warmup)
+        ts[S_new] = att(per)
+        del r, t
+    pad = ps.B * (8448 - ps.S)
+    fill_bytes = pad * (2 * w.Hq * w.D * 2 + 2 * w.Hkv * w.D * 2 + w.Hq * 4)  # O, dQ, dK, dV, LSE of pad rows
+    fill_ms = fill_bytes / (copy_gbps * 1e9 / 2) * 1e3  # writes at half the copy (read + write) rate
+    extra_ms = ts[8448] - ts[ps.S] - fill_ms
+    return {"workload": "response_long 4 x 4352 vs rows padded to 8448", "attn_ms": ts[ps.S], "attn_ms_padded": ts[8448],
+            "pad_output_bytes": fill_bytes, "predicted_fill_ms": fill_ms, "excess_ms": extra_ms,
+            "excess_frac": extra_ms / ts[ps.S]}
+
+
 def cpu_baseline(w, seconds):
     """The fp64 oracle (dense masked attention + naive backward) on a bounded
     sample of the same workload: whole (batch row, kv group) units, in order,
@@ -284,6 +349,17 @@ def main():
             "pairwise_layout": {"B": pps.B, "S": pps.S, "allowed_pairs": allowed_pairs(pps)},
         })
         log(f"dense-map attn {att(per_d):.3f} ms, pairwise attn {att(per_p):.3f} ms, sparse attn {att(per):.3f} ms")
+
+    peak_meas = measured_mfma_peak(A, torch)
+    extra["measured_mfma_peak_tflops"] = peak_meas
+    extra["frac_of_measured_peak"] = value / peak_meas
+    roofline["frac_of_measured_peak"] = achieved / peak_meas
+    log(f"measured MFMA peak {peak_meas:.0f} TFLOP/s: step at {value / peak_meas:.3f}, {dom} at {achieved / peak_meas:.3f}")
+    if not args.no_baselines:
+        gbps = copy_bandwidth(torch)
+        extra["copy_GBps"] = gbps
+        extra["skip_cost"] = skip_cost(A, torch, max(5, args.steps // 2), 2, gbps)
+        log(f"skip cost: {json.dumps(extra['skip_cost'])}")
 
     if args.copy_calibration:
         # 2^28 bytes read and 2^28 bytes written per launch, 3 launches.

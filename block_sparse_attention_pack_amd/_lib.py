@@ -26,7 +26,7 @@ PBA_OK = 0
 TILE_SKIP, TILE_PARTIAL, TILE_FULL = 0, 1, 2
 EXPORTED = ("pba_strerror", "pba_fwd_tile", "pba_bwd_tile", "pba_map_bytes", "pba_map_init",
             "pba_pack_block_map", "pba_pack_block_maps", "pba_packed_attn_fwd", "pba_bwd_workspace_bytes", "pba_packed_attn_bwd",
-            "pba_packed_attn_bwd_stages")
+            "pba_packed_attn_bwd_stages", "pba_mfma_probe")
 
 
 class PbaBlockMap(ctypes.Structure):
@@ -68,6 +68,8 @@ _lib.pba_packed_attn_bwd.argtypes = [ctypes.POINTER(PbaBlockMap)] * 2 + [ctypes.
 _lib.pba_packed_attn_bwd.restype = ctypes.c_int
 _lib.pba_packed_attn_bwd_stages.argtypes = [ctypes.c_int] + list(_lib.pba_packed_attn_bwd.argtypes)
 _lib.pba_packed_attn_bwd_stages.restype = ctypes.c_int
+_lib.pba_mfma_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+_lib.pba_mfma_probe.restype = ctypes.c_int
 BWD_DQ, BWD_DKDV, BWD_ALL = 1, 2, 3
 
 
@@ -270,3 +272,15 @@ def packed_attn_bwd(qmap: BlockMap, kmap: BlockMap, q, k, v, o, lse, dout, softm
                                            workspace.numel() - off, B, S, Hq, Hkv, D, scale, _stream(stream)),
            "pba_packed_attn_bwd_stages")
     return dq, dk, dv
+
+
+# FLOP of one pba_mfma_probe iteration per workgroup: 4 waves x 16 MFMAs x 32x32x16x2.
+MFMA_PROBE_FLOP_PER_BLOCK_ITER = 4 * 16 * 32 * 32 * 16 * 2
+
+
+def mfma_probe(out: torch.Tensor, n_blocks: int, iters: int, stream=None) -> None:
+    """Enqueue the library's sustained-MFMA-rate loop (a measurement helper);
+    `out` is a float32 device tensor of at least n_blocks * 256 elements."""
+    if out.dtype != torch.float32 or out.numel() < n_blocks * 256 or not out.is_cuda:
+        raise ValueError("out must be a float32 device tensor of n_blocks * 256 elements")
+    _check(_lib.pba_mfma_probe(out.data_ptr(), n_blocks, iters, _stream(stream)), "pba_mfma_probe")

@@ -312,3 +312,18 @@ int pba_packed_attn_bwd(const pba_block_map* qmap, const pba_block_map* kmap, co
 }
 
 }  // extern "C"
+
+namespace pba {
+hipError_t launch_mfma_probe(float* out, int n_blocks, int iters, hipStream_t stream);  // pba_probe.hip
+}
+
+extern "C" {
+
+int pba_mfma_probe(float* out, int n_blocks, int iters, void* stream) {
+  if (!out) return PBA_ERR_NULL;
+  if (n_blocks < 1 || n_blocks > (1 << 20) || iters < 1) return PBA_ERR_SHAPE;
+  if (int rc = device_ok()) return rc;
+  return pba::launch_mfma_probe(out, n_blocks, iters, (hipStream_t)stream) == hipSuccess ? PBA_OK : PBA_ERR_DEVICE;
+}
+
+}  // extern "C"

@@ -223,6 +223,16 @@ PBA_API int pba_packed_attn_bwd_stages(int stages, const pba_block_map* qmap, co
                                        size_t workspace_bytes, int B, int S, int Hq, int Hkv, int D,
                                        float softmax_scale, void* stream);
 
+/* Measurement helper, not an operation of the method: enqueues n_blocks
+ * workgroups of 256 threads that each run `iters` iterations of 16 bf16
+ * MFMAs (v_mfma_f32_32x32x16_bf16, 32768 FLOP each) per wave, i.e.
+ * n_blocks * 4 * iters * 16 * 32768 FLOP, and write one float per thread
+ * to `out` (device, caller-allocated, n_blocks * 256 floats).  Timing it
+ * gives the sustained MFMA rate of the device.  Returns PBA_OK,
+ * PBA_ERR_NULL, PBA_ERR_SHAPE (n_blocks outside 1..2^20 or iters < 1) or
+ * PBA_ERR_DEVICE. */
+PBA_API int pba_mfma_probe(float* out, int n_blocks, int iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
