@@ -16,6 +16,8 @@ method equals ordinary masked softmax attention):
   segments.block_map     brute-force tile classification and visit lists
   attention.attn_fwd / attn_bwd   dense fp64 masked attention and its naive
                          backward (softmax Jacobian), per row and q-head
+  positions.positions    aligned position ids, log-prob gather rows and the
+                         response loss mask from descriptors
 
 Every function is pinned in tests/ against facts the pages or mathematics
 fix (worked masks, closed-form counts, brute force, finite differences,
@@ -27,3 +29,4 @@ from .segments import (  # noqa: F401
 from .attention import (  # noqa: F401
     attn_fwd, attn_bwd, attn_fwd_rows, attn_bwd_sampled, useful_flops,
 )
+from .positions import positions  # noqa: F401
