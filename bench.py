@@ -350,6 +350,24 @@ def main():
         })
         log(f"dense-map attn {att(per_d):.3f} ms, pairwise attn {att(per_p):.3f} ms, sparse attn {att(per):.3f} ms")
 
+    # Aligned positions / log-prob gather rows (a next step on the same map, reported beside the step).
+    pos_out = (torch.empty((ps.B, ps.S), dtype=torch.int32, device=dev),
+               torch.empty((ps.B, ps.S), dtype=torch.int32, device=dev),
+               torch.empty((ps.B, ps.S), dtype=torch.uint8, device=dev))
+    for _ in range(3):
+        A.pack_positions(r.fmap, out=pos_out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        A.pack_positions(r.fmap, out=pos_out)
+    e1.record()
+    torch.cuda.synchronize()
+    pos_ms = e0.elapsed_time(e1) / 20
+    pos_bytes = ps.B * ps.S * (4 + 4 + 16 + 4 + 4 + 1)
+    extra["positions"] = {"ms": pos_ms, "GBps": pos_bytes / (pos_ms * 1e-3) / 1e9, "bytes": pos_bytes}
+    log(f"positions {pos_ms * 1e3:.1f} us")
+
     peak_meas = measured_mfma_peak(A, torch)
     extra["measured_mfma_peak_tflops"] = peak_meas
     extra["frac_of_measured_peak"] = value / peak_meas

@@ -26,7 +26,7 @@ PBA_OK = 0
 TILE_SKIP, TILE_PARTIAL, TILE_FULL = 0, 1, 2
 EXPORTED = ("pba_strerror", "pba_fwd_tile", "pba_bwd_tile", "pba_map_bytes", "pba_map_init",
             "pba_pack_block_map", "pba_pack_block_maps", "pba_packed_attn_fwd", "pba_bwd_workspace_bytes", "pba_packed_attn_bwd",
-            "pba_packed_attn_bwd_stages", "pba_mfma_probe")
+            "pba_packed_attn_bwd_stages", "pba_mfma_probe", "pba_pack_positions")
 
 
 class PbaBlockMap(ctypes.Structure):
@@ -68,6 +68,8 @@ _lib.pba_packed_attn_bwd.argtypes = [ctypes.POINTER(PbaBlockMap)] * 2 + [ctypes.
 _lib.pba_packed_attn_bwd.restype = ctypes.c_int
 _lib.pba_packed_attn_bwd_stages.argtypes = [ctypes.c_int] + list(_lib.pba_packed_attn_bwd.argtypes)
 _lib.pba_packed_attn_bwd_stages.restype = ctypes.c_int
+_lib.pba_pack_positions.argtypes = [ctypes.POINTER(PbaBlockMap)] + [ctypes.c_void_p] * 4
+_lib.pba_pack_positions.restype = ctypes.c_int
 _lib.pba_mfma_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
 _lib.pba_mfma_probe.restype = ctypes.c_int
 BWD_DQ, BWD_DKDV, BWD_ALL = 1, 2, 3
@@ -284,3 +286,19 @@ def mfma_probe(out: torch.Tensor, n_blocks: int, iters: int, stream=None) -> Non
     if out.dtype != torch.float32 or out.numel() < n_blocks * 256 or not out.is_cuda:
         raise ValueError("out must be a float32 device tensor of n_blocks * 256 elements")
     _check(_lib.pba_mfma_probe(out.data_ptr(), n_blocks, iters, _stream(stream)), "pba_mfma_probe")
+
+
+def pack_positions(m: BlockMap, out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None, stream=None):
+    """(pos_ids int32 [B,S], src_row int32 [B,S], loss_mask uint8 [B,S]) of a
+    built map: aligned positions, the row whose logits predict each token,
+    and the response tokens that enter the log-prob sums."""
+    if out is None:
+        pos = torch.empty((m.B, m.S), dtype=torch.int32, device="cuda")
+        src = torch.empty((m.B, m.S), dtype=torch.int32, device="cuda")
+        mask = torch.empty((m.B, m.S), dtype=torch.uint8, device="cuda")
+    else:
+        pos, src, mask = out
+    ptr = lambda x: None if x is None else x.data_ptr()  # noqa: E731
+    _check(_lib.pba_pack_positions(ctypes.byref(m.struct), ptr(pos), ptr(src), ptr(mask), _stream(stream)),
+           "pba_pack_positions")
+    return pos, src, mask

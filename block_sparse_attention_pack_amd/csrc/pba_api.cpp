@@ -219,6 +219,25 @@ int pba_pack_block_maps(const pba_pack* packs, int n_packs, const int32_t* resp_
   return e == hipSuccess ? PBA_OK : PBA_ERR_DEVICE;
 }
 
+int pba_pack_positions(const pba_block_map* map, int32_t* pos_ids, int32_t* src_row, uint8_t* loss_mask,
+                       void* stream) {
+  if (!map || !map->tok_pack || !map->tok_branch || !map->tok_win || !map->status) return PBA_ERR_NULL;
+  if (map->B < 1 || map->B > kMaxB || map->S < 1 || map->S > kMaxS) return PBA_ERR_SHAPE;
+  if (!pos_ids && !src_row && !loss_mask) return PBA_OK;
+  if (int rc = device_ok()) return rc;
+  pba::PosArgs a;
+  a.ntok = (int64_t)map->B * map->S;
+  a.S = map->S;
+  a.status = map->status;
+  a.tok_pack = map->tok_pack;
+  a.tok_branch = map->tok_branch;
+  a.tok_win = map->tok_win;
+  a.pos = pos_ids;
+  a.src = src_row;
+  a.mask = loss_mask;
+  return pba::launch_positions(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PBA_OK : PBA_ERR_DEVICE;
+}
+
 int pba_pack_block_map(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,
                        const pba_block_map* map, void* stream) {
   return pba_pack_block_maps(packs, n_packs, resp_len, n_resp_total, map, 1, stream);

@@ -23,6 +23,8 @@
 //   map_lists     one wave per list: ballot compaction, full then partial
 //   map_order     one block per (side, map): stable sort of the tiles by
 //                 visit count, descending
+//   map_positions (its own entry point, on a built map) aligned position
+//                 ids, log-prob gather rows and the response loss mask
 #include "pba_internal.h"
 
 namespace pba {
@@ -351,7 +353,39 @@ __global__ void __launch_bounds__(kOrderThreads) map_order(MapSet ms) {
   }
 }
 
+// Aligned positions and log-prob gather rows from the per-token windows
+// ("DPO Preference Packing: Dense Masks and Sparse Execution", section
+// "Layout requirements": a response token keeps the position and the
+// predicting row it has in its own [prompt | response] sequence, so a
+// response's first token reads the last prompt row; "Pack training sequences
+// to reduce padding waste": positions restart and no target crosses an
+// example boundary).  Token s sees [pre_lo, pre_hi) U [kv_lo, s]: its
+// sequence so far is the prompt run (if separate) then [kv_lo, s], so its
+// position is (pre_hi - pre_lo) + (s - kv_lo) and its predecessor s - 1
+// inside [kv_lo, s], else pre_hi - 1, else none.  One thread per token.
+__global__ void __launch_bounds__(kThreads) map_positions(PosArgs a) {
+  if (a.status[0] != 0) return;
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (t >= a.ntok) return;
+  const int s = (int)(t % a.S);
+  const int br = a.tok_branch[t];
+  const int4 w = reinterpret_cast<const int4*>(a.tok_win)[t];
+  const bool pad = a.tok_pack[t] < 0;
+  const int pre = w.z - w.y;
+  const int pos = pad ? 0 : pre + (s - w.x);
+  const int src = pad ? -1 : (s > w.x ? s - 1 : (pre > 0 ? w.z - 1 : -1));
+  if (a.pos) a.pos[t] = pos;
+  if (a.src) a.src[t] = src;
+  if (a.mask) a.mask[t] = (uint8_t)(br > 0 && src >= 0);
+}
+
 }  // namespace
+
+hipError_t launch_positions(const PosArgs& a, hipStream_t stream) {
+  if (a.ntok <= 0) return hipSuccess;
+  map_positions<<<(unsigned)((a.ntok + kThreads - 1) / kThreads), kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_maps(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,
                        const pba_block_map* maps, int n_maps, hipStream_t stream) {

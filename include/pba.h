@@ -175,6 +175,30 @@ PBA_API int pba_pack_block_map(const pba_pack* packs, int n_packs, const int32_t
 PBA_API int pba_pack_block_maps(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,
                                 const pba_block_map* maps, int n_maps, void* stream);
 
+/* Aligned position ids, log-prob gather rows and the response loss mask of
+ * a packed batch ("DPO Preference Packing: Dense Masks and Sparse
+ * Execution", section "Layout requirements": response tokens keep the
+ * position ids of their own prompt + response sequence, and log-probs are
+ * gathered from the logits that predict each response token, a response's
+ * first token from the final prompt row; "Pack training sequences to reduce
+ * padding waste", sections on target boundaries and position IDs).
+ * From a map built by pba_pack_block_map(s) (any tile shape), for token s
+ * of row b (device arrays of B*S elements, caller-allocated; any of them
+ * may be NULL and is then not written):
+ *   pos_ids[b*S+s]   prompt token j -> j; token t of a response ->
+ *                    prompt_len + t; 0 for pad
+ *   src_row[b*S+s]   position in row b of the token whose logits predict
+ *                    token s: s-1 inside a prompt or response, the last
+ *                    prompt token for a response's first token, -1 when
+ *                    there is none (a pack's first token, a response's
+ *                    first token after an empty prompt, pad)
+ *   loss_mask[b*S+s] 1 for a response token with src_row >= 0, else 0
+ * Enqueued on `stream` after the map build; nothing is written when the
+ * map's status is not OK.  Returns PBA_OK, PBA_ERR_NULL (map or its token
+ * arrays), PBA_ERR_SHAPE or PBA_ERR_DEVICE. */
+PBA_API int pba_pack_positions(const pba_block_map* map, int32_t* pos_ids, int32_t* src_row, uint8_t* loss_mask,
+                               void* stream);
+
 /* Forward.  For every query token and q head: O = softmax(scale * Q K^T
  * restricted to the allowed keys) V, and LSE = natural log of the sum of
  * exp(scale * q.k) over the allowed keys (the softmax normaliser, kept for

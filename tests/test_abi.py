@@ -85,3 +85,19 @@ def test_host_argument_errors():
     assert lib.pba_packed_attn_bwd(*args, 256, ws, 2, 100, 4, 2, 64, float("inf"), None) == -10
     # one batch row of Q must stay under 2 GiB (32-bit buffer offsets)
     assert lib.pba_packed_attn_fwd(ctypes.byref(m), 16, 16, 16, 16, 16, 2, 1 << 20, 16, 8, 128, 0.1, None) == -2
+
+
+def test_positions_and_probe_argument_errors():
+    import block_sparse_attention_pack_amd as P
+    A = P.api
+    lib = A._lib
+    assert lib.pba_pack_positions(None, 16, 16, 16, None) == -1
+    m = A.PbaBlockMap()
+    assert lib.pba_map_init(ctypes.byref(m), 256, 1 << 20, 2, 100, 64, 64) == 0
+    # nothing requested: nothing to do, no device needed
+    assert lib.pba_pack_positions(ctypes.byref(m), None, None, None, None) == 0
+    bad = A.PbaBlockMap()
+    assert lib.pba_pack_positions(ctypes.byref(bad), 16, None, None, None) == -1
+    assert lib.pba_mfma_probe(None, 1, 1, None) == -1
+    assert lib.pba_mfma_probe(16, 0, 1, None) == -2
+    assert lib.pba_mfma_probe(16, 1, 0, None) == -2
