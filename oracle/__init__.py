@@ -18,6 +18,8 @@ method equals ordinary masked softmax attention):
                          backward (softmax Jacobian), per row and q-head
   positions.positions    aligned position ids, log-prob gather rows and the
                          response loss mask from descriptors
+  logprob.token_logp / response_logp   log-softmax at the gather rows and
+                         per-response sums
 
 Every function is pinned in tests/ against facts the pages or mathematics
 fix (worked masks, closed-form counts, brute force, finite differences,
@@ -30,3 +32,4 @@ from .attention import (  # noqa: F401
     attn_fwd, attn_bwd, attn_fwd_rows, attn_bwd_sampled, useful_flops,
 )
 from .positions import positions  # noqa: F401
+from .logprob import row_logsumexp, token_logp, response_logp  # noqa: F401
