@@ -215,6 +215,34 @@ def skip_cost(A, torch, steps, warmup, copy_gbps):
             "excess_frac": extra_ms / ts[ps.S]}
 
 
+def logp_rate(A, torch, r, pos_out, ps, V=151936):
+    """Time pba_packed_token_logp on bf16 logits [B, S, V] (seeded normal,
+    std 2.5) for the workload's response tokens: HBM bytes = one logits row
+    (2 V bytes) per loss term, the rest is negligible."""
+    g = torch.Generator(device="cuda").manual_seed(0)
+    logits = (torch.randn((ps.B, ps.S, V), generator=g, device="cuda", dtype=torch.float32) * 2.5).to(torch.bfloat16)
+    tokens = torch.randint(0, V, (ps.B, ps.S), generator=g, device="cuda", dtype=torch.int32)
+    _, src, mask = pos_out
+    tok = torch.empty((ps.B, ps.S), dtype=torch.float32, device="cuda")
+    resp = torch.empty(r.R.numel(), dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        A.packed_token_logp(r.fmap, src, mask, logits, tokens, r.P, r.R, out=(tok, resp))
+    torch.cuda.synchronize()
+    n = 10
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        A.packed_token_logp(r.fmap, src, mask, logits, tokens, r.P, r.R, out=(tok, resp))
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    terms = int(mask.sum())
+    nbytes = terms * V * 2
+    del logits
+    return {"vocab": V, "loss_terms": terms, "ms": ms, "hbm_bytes": nbytes,
+            "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
 def cpu_baseline(w, seconds):
     """The fp64 oracle (dense masked attention + naive backward) on a bounded
     sample of the same workload: whole (batch row, kv group) units, in order,
@@ -367,6 +395,10 @@ def main():
     pos_bytes = ps.B * ps.S * (4 + 4 + 16 + 4 + 4 + 1)
     extra["positions"] = {"ms": pos_ms, "GBps": pos_bytes / (pos_ms * 1e-3) / 1e9, "bytes": pos_bytes}
     log(f"positions {pos_ms * 1e3:.1f} us")
+
+    # Packed token log-probs over a Qwen3-sized vocabulary (a next step after attention, reported beside the step).
+    extra["logp"] = logp_rate(A, torch, r, pos_out, ps)
+    log(f"token log-probs: {json.dumps(extra['logp'])}")
 
     peak_meas = measured_mfma_peak(A, torch)
     extra["measured_mfma_peak_tflops"] = peak_meas

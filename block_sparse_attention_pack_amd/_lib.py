@@ -26,7 +26,8 @@ PBA_OK = 0
 TILE_SKIP, TILE_PARTIAL, TILE_FULL = 0, 1, 2
 EXPORTED = ("pba_strerror", "pba_fwd_tile", "pba_bwd_tile", "pba_map_bytes", "pba_map_init",
             "pba_pack_block_map", "pba_pack_block_maps", "pba_packed_attn_fwd", "pba_bwd_workspace_bytes", "pba_packed_attn_bwd",
-            "pba_packed_attn_bwd_stages", "pba_mfma_probe", "pba_pack_positions")
+            "pba_packed_attn_bwd_stages", "pba_mfma_probe", "pba_pack_positions",
+            "pba_packed_token_logp")
 
 
 class PbaBlockMap(ctypes.Structure):
@@ -70,6 +71,10 @@ _lib.pba_packed_attn_bwd_stages.argtypes = [ctypes.c_int] + list(_lib.pba_packed
 _lib.pba_packed_attn_bwd_stages.restype = ctypes.c_int
 _lib.pba_pack_positions.argtypes = [ctypes.POINTER(PbaBlockMap)] + [ctypes.c_void_p] * 4
 _lib.pba_pack_positions.restype = ctypes.c_int
+_lib.pba_packed_token_logp.argtypes = [ctypes.POINTER(PbaBlockMap), ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+_lib.pba_packed_token_logp.restype = ctypes.c_int
 _lib.pba_mfma_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
 _lib.pba_mfma_probe.restype = ctypes.c_int
 BWD_DQ, BWD_DKDV, BWD_ALL = 1, 2, 3
@@ -302,3 +307,29 @@ def pack_positions(m: BlockMap, out: Optional[Tuple[torch.Tensor, torch.Tensor, 
     _check(_lib.pba_pack_positions(ctypes.byref(m.struct), ptr(pos), ptr(src), ptr(mask), _stream(stream)),
            "pba_pack_positions")
     return pos, src, mask
+
+
+def packed_token_logp(m: BlockMap, src_row, loss_mask, logits, tokens, packs_dev=None, resp_len_dev=None,
+                      out: Optional[Tuple[torch.Tensor, Optional[torch.Tensor]]] = None, stream=None):
+    """(tok_logp fp32 [B,S], resp_logp fp32 [n_resp] or None): log-softmax of
+    each response token's predicting row at its token id, and the
+    per-response sums (when the descriptors are given)."""
+    if logits.dtype != torch.bfloat16 or logits.dim() != 3 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous bf16 [B, S, V] tensor")
+    B, S, V = logits.shape
+    if (B, S) != (m.B, m.S):
+        raise ValueError("logits do not match the map's rows")
+    if out is None:
+        tok = torch.empty((B, S), dtype=torch.float32, device=logits.device)
+        resp = None if packs_dev is None else torch.empty(resp_len_dev.numel(), dtype=torch.float32,
+                                                          device=logits.device)
+    else:
+        tok, resp = out
+    n_packs = 0 if packs_dev is None else packs_dev.shape[0]
+    n_resp = 0 if resp_len_dev is None else resp_len_dev.numel()
+    ptr = lambda x: None if x is None else x.data_ptr()  # noqa: E731
+    _check(_lib.pba_packed_token_logp(ctypes.byref(m.struct), ptr(packs_dev), n_packs, ptr(resp_len_dev), n_resp,
+                                      src_row.data_ptr(), loss_mask.data_ptr(), logits.data_ptr(), V,
+                                      tokens.data_ptr(), tok.data_ptr(), ptr(resp), _stream(stream)),
+           "pba_packed_token_logp")
+    return tok, resp

@@ -6,7 +6,7 @@
 #include <cstring>
 #include <mutex>
 
-#include "pba_internal.h"
+#include "pba_next.h"
 
 namespace {
 
@@ -236,6 +236,41 @@ int pba_pack_positions(const pba_block_map* map, int32_t* pos_ids, int32_t* src_
   a.src = src_row;
   a.mask = loss_mask;
   return pba::launch_positions(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PBA_OK : PBA_ERR_DEVICE;
+}
+
+int pba_packed_token_logp(const pba_block_map* map, const pba_pack* packs, int n_packs, const int32_t* resp_len,
+                          int n_resp_total, const int32_t* src_row, const uint8_t* loss_mask, const void* logits,
+                          int V, const int32_t* tokens, float* tok_logp, float* resp_logp, void* stream) {
+  if (!map || !map->status || !src_row || !loss_mask || !logits || !tokens || !tok_logp) return PBA_ERR_NULL;
+  if (map->B < 1 || map->B > kMaxB || map->S < 1 || map->S > kMaxS) return PBA_ERR_SHAPE;
+  if (V < 8 || V % 8 != 0) return PBA_ERR_SHAPE;
+  if (!aligned16(logits)) return PBA_ERR_ALIGN;
+  if (resp_logp) {
+    if (n_packs < 0 || n_resp_total < 0) return PBA_ERR_SHAPE;
+    if ((n_packs > 0 && !packs) || (n_resp_total > 0 && !resp_len)) return PBA_ERR_NULL;
+  }
+  if (int rc = device_ok()) return rc;
+  pba::LogpArgs a;
+  a.status = map->status;
+  a.logits = static_cast<const pba::bf16*>(logits);
+  a.V = V;
+  a.ntok = (int64_t)map->B * map->S;
+  a.S = map->S;
+  a.tokens = tokens;
+  a.src = src_row;
+  a.mask = loss_mask;
+  a.tok_logp = tok_logp;
+  pba::RespSumArgs r;
+  r.status = map->status;
+  r.packs = packs;
+  r.n_packs = n_packs;
+  r.S = map->S;
+  r.resp_len = resp_len;
+  r.tok_logp = tok_logp;
+  r.resp_logp = resp_logp;
+  return pba::launch_token_logp(a, resp_logp ? &r : nullptr, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PBA_OK
+             : PBA_ERR_DEVICE;
 }
 
 int pba_pack_block_map(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,

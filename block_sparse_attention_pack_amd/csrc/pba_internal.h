@@ -69,19 +69,6 @@ constexpr float kLog2eHost = 1.4426950408889634f;
 
 // Launchers (return hipError_t of the launch).
 constexpr int kMaxMapsPerBuild = PBA_MAX_MAPS_PER_BUILD;
-struct PosArgs {  // map_positions
-  int64_t ntok;
-  int S;
-  const int32_t* status;
-  const int32_t* tok_pack;
-  const int32_t* tok_branch;
-  const int32_t* tok_win;
-  int32_t* pos;
-  int32_t* src;
-  uint8_t* mask;
-};
-hipError_t launch_positions(const PosArgs& a, hipStream_t stream);
-
 hipError_t launch_maps(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,
                        const pba_block_map* maps, int n_maps, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int D, int B, hipStream_t stream);

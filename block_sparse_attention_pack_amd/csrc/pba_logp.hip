@@ -1,0 +1,143 @@
+// Packed token log-probs ("DPO Preference Packing: Dense Masks and Sparse
+// Execution", section "Layout requirements": a response's log-prob is
+// gathered from the logits that predict each of its tokens, a response's
+// first token from the final prompt row).  With the gather rows and the
+// response loss mask of map_positions:
+//
+//   tok_logp[t] = x[y] - log sum_v exp(x[v]),  x = logits[b, src_row[t], :],
+//                 y = tokens[t]                 (loss_mask[t] = 1; else 0)
+//   resp_logp[i] = sum of tok_logp over response i's tokens, in token order
+//
+//   token_logp  one workgroup per token: streams its predicting row (V bf16,
+//               16 bytes per lane per load, four loads in flight) through an
+//               online log-sum-exp in the log2 domain, fp32; bound by HBM
+//               (2 bytes per logit read once)
+//   resp_logp   one wave per pack: each response's sum with a fixed reduction
+//               order (deterministic)
+#include "pba_next.h"
+#include "pba_tile.h"
+
+namespace pba {
+namespace {
+
+constexpr int kLpThreads = 256;
+constexpr int kUnroll = 4;
+
+struct LseAcc {
+  float m;  // running max, log2 domain
+  float s;  // sum of 2^(t - m)
+};
+
+__device__ __forceinline__ LseAcc lse_merge(LseAcc a, LseAcc b) {
+  const float m = fmaxf(a.m, b.m);
+  if (m == -__builtin_inff()) return {m, 0.f};
+  return {m, a.s * fast_exp2(a.m - m) + b.s * fast_exp2(b.m - m)};
+}
+
+__device__ __forceinline__ float bf16_lo(unsigned u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
+
+__global__ void __launch_bounds__(kLpThreads) token_logp(LogpArgs a) {
+  if (a.status[0] != 0) return;
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (!a.mask[t]) {
+    if (tid == 0) a.tok_logp[t] = 0.f;
+    return;
+  }
+  const int64_t b = t / a.S;
+  const int r = min(max(a.src[t], 0), a.S - 1);  // a valid map gives 0 <= src < S here
+  const u32x4* row = reinterpret_cast<const u32x4*>(a.logits + (b * a.S + r) * a.V);
+  const int nch = (int)(a.V / 8);
+  LseAcc acc = {-__builtin_inff(), 0.f};
+  int c = tid;
+  // Four 16-byte loads in flight per lane, then their 32 logits.
+  for (; c + (kUnroll - 1) * kLpThreads < nch; c += kUnroll * kLpThreads) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = row[c + u * kLpThreads];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float x[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[2 * k] = bf16_lo(v[u][k]);
+        x[2 * k + 1] = bf16_hi(v[u][k]);
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int k = 1; k < 8; ++k) mx = fmaxf(mx, x[k]);
+      const float nm = fmaxf(acc.m, mx * kLog2e);
+      float s = acc.s * fast_exp2(acc.m - nm);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s += fast_exp2(__builtin_fmaf(x[k], kLog2e, -nm));
+      acc = {nm, s};
+    }
+  }
+  for (; c < nch; c += kLpThreads) {
+    const u32x4 v = row[c];
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = bf16_lo(v[k]);
+      x[2 * k + 1] = bf16_hi(v[k]);
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) mx = fmaxf(mx, x[k]);
+    const float nm = fmaxf(acc.m, mx * kLog2e);
+    float s = acc.s * fast_exp2(acc.m - nm);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += fast_exp2(__builtin_fmaf(x[k], kLog2e, -nm));
+    acc = {nm, s};
+  }
+  // Workgroup reduction of (max, sum): within each wave, then across waves.
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const LseAcc o = {__shfl_xor(acc.m, off), __shfl_xor(acc.s, off)};
+    acc = lse_merge(acc, o);
+  }
+  __shared__ LseAcc part[kLpThreads / 64];
+  if ((tid & 63) == 0) part[tid >> 6] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    LseAcc all = part[0];
+#pragma unroll
+    for (int w = 1; w < kLpThreads / 64; ++w) all = lse_merge(all, part[w]);
+    const int y = a.tokens[t];
+    const bool ok = y >= 0 && (int64_t)y < a.V;
+    const unsigned short bits = reinterpret_cast<const unsigned short*>(row)[ok ? y : 0];
+    const float xy = __uint_as_float((unsigned)bits << 16);
+    a.tok_logp[t] = ok ? xy - (all.m + __log2f(all.s)) * kLn2 : __builtin_nanf("");
+  }
+}
+
+__global__ void __launch_bounds__(kLpThreads) resp_logp(RespSumArgs a) {
+  if (a.status[0] != 0) return;
+  const int p = blockIdx.x * (kLpThreads / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (p >= a.n_packs) return;
+  const pba_pack pk = a.packs[p];
+  const int64_t base = (int64_t)pk.row * a.S;
+  int rs = pk.start + pk.prompt_len;
+  for (int k = 0; k < pk.n_resp; ++k) {
+    const int len = a.resp_len[pk.resp_first + k];
+    float s = 0.f;
+    for (int i = lane; i < len; i += 64) s += a.tok_logp[base + rs + i];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) a.resp_logp[pk.resp_first + k] = s;
+    rs += len;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_token_logp(const LogpArgs& a, const RespSumArgs* r, hipStream_t stream) {
+  if (a.ntok > 0) token_logp<<<(unsigned)a.ntok, kLpThreads, 0, stream>>>(a);
+  if (r && r->n_packs > 0)
+    resp_logp<<<(unsigned)((r->n_packs + kLpThreads / 64 - 1) / (kLpThreads / 64)), kLpThreads, 0, stream>>>(*r);
+  return hipGetLastError();
+}
+
+}  // namespace pba

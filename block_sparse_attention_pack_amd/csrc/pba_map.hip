@@ -25,7 +25,7 @@
 //                 visit count, descending
 //   map_positions (its own entry point, on a built map) aligned position
 //                 ids, log-prob gather rows and the response loss mask
-#include "pba_internal.h"
+#include "pba_next.h"
 
 namespace pba {
 namespace {

@@ -199,6 +199,28 @@ PBA_API int pba_pack_block_maps(const pba_pack* packs, int n_packs, const int32_
 PBA_API int pba_pack_positions(const pba_block_map* map, int32_t* pos_ids, int32_t* src_row, uint8_t* loss_mask,
                                void* stream);
 
+/* Packed token log-probs and per-response sums ("DPO Preference Packing:
+ * Dense Masks and Sparse Execution", section "Layout requirements": a
+ * response's log-prob is gathered from the logits that predict each of its
+ * tokens, including the branch start).  With src_row and loss_mask from
+ * pba_pack_positions on the same map, for every token t = b*S+s:
+ *   tok_logp[t] = logits[b, src_row[t], y] - log sum_v exp(logits[b, src_row[t], v]),
+ *                 y = tokens[t], where loss_mask[t] = 1; 0 where it is 0;
+ *                 NaN when y is outside [0, V)
+ * (fp32 accumulation), and, if resp_logp is not NULL, for every response i
+ * of the descriptors (indexed like resp_len), resp_logp[i] = the sum of
+ * tok_logp over its tokens in token order (deterministic).
+ * logits: bf16 [B, S, V] device, 16-byte aligned, V a multiple of 8;
+ * tokens int32 [B*S]; tok_logp fp32 [B*S]; resp_logp fp32 [n_resp_total];
+ * packs / resp_len as given to the map build (needed only for resp_logp).
+ * Enqueued on `stream`; nothing is written when the map's status is not OK.
+ * Returns PBA_OK, PBA_ERR_NULL, PBA_ERR_SHAPE (B, S, V or counts),
+ * PBA_ERR_ALIGN or PBA_ERR_DEVICE. */
+PBA_API int pba_packed_token_logp(const pba_block_map* map, const pba_pack* packs, int n_packs,
+                                  const int32_t* resp_len, int n_resp_total, const int32_t* src_row,
+                                  const uint8_t* loss_mask, const void* logits, int V, const int32_t* tokens,
+                                  float* tok_logp, float* resp_logp, void* stream);
+
 /* Forward.  For every query token and q head: O = softmax(scale * Q K^T
  * restricted to the allowed keys) V, and LSE = natural log of the sum of
  * exp(scale * q.k) over the allowed keys (the softmax normaliser, kept for
