@@ -22,7 +22,8 @@
 //                 visible pairs of every key tile from the query windows
 //   map_lists     one wave per list: ballot compaction, full then partial
 //   map_order     one block per (side, map): stable sort of the tiles by
-//                 visit count, descending
+//                 visit count, descending (bitonic sort in LDS up to 2048
+//                 tiles per side, a counting sort through the work area beyond)
 //   map_positions (its own entry point, on a built map) aligned position
 //                 ids, log-prob gather rows and the response loss mask
 #include "pba_next.h"
@@ -193,19 +194,36 @@ __global__ void __launch_bounds__(kThreads) map_classify(MapSet ms) {
     win[r] = i < S ? reinterpret_cast<const int4*>(m.tok_win)[(int64_t)b * S + i] : make_int4(i + 1, 0, 0, i);
   }
   __syncthreads();
+  // Key tiles in chunks of up to 256; a chunk's rows are split among the
+  // threads that the chunk leaves free (rc row slices per key tile), and the
+  // slices' counts meet in LDS.
+  __shared__ int tc[kThreads];
   int nf = 0, np = 0, ns = 0;
-  for (int kt = threadIdx.x; kt < nkt; kt += kThreads) {
-    const int k0 = kt * bn, k1 = k0 + bn;
-    int c = 0;
-    for (int r = 0; r < bm; ++r) {
-      const int4 w = win[r];
-      c += overlap(w.y, w.z, k0, k1) + overlap(w.x, q0 + r + 1, k0, k1);
+  for (int kc = 0; kc < nkt; kc += kThreads) {
+    const int nk = min(nkt - kc, kThreads);
+    const int rc = max(1, min(kThreads / nk, bm));
+    for (int i = threadIdx.x; i < nk; i += kThreads) tc[i] = 0;
+    __syncthreads();
+    if (threadIdx.x < nk * rc) {
+      const int kl = threadIdx.x % nk, slice = threadIdx.x / nk;
+      const int k0 = (kc + kl) * bn, k1 = k0 + bn;
+      int c = 0;
+      for (int r = slice * bm / rc; r < (slice + 1) * bm / rc; ++r) {
+        const int4 w = win[r];
+        c += overlap(w.y, w.z, k0, k1) + overlap(w.x, q0 + r + 1, k0, k1);
+      }
+      atomicAdd(&tc[kl], c);
     }
-    const int v = c == bm * bn ? PBA_TILE_FULL : (c == 0 ? PBA_TILE_SKIP : PBA_TILE_PARTIAL);
-    m.cls[((int64_t)b * nqt + qt) * nkt + kt] = (uint8_t)v;
-    nf += v == PBA_TILE_FULL;
-    np += v == PBA_TILE_PARTIAL;
-    ns += v == PBA_TILE_SKIP;
+    __syncthreads();
+    for (int kl = threadIdx.x; kl < nk; kl += kThreads) {
+      const int c = tc[kl];
+      const int v = c == bm * bn ? PBA_TILE_FULL : (c == 0 ? PBA_TILE_SKIP : PBA_TILE_PARTIAL);
+      m.cls[((int64_t)b * nqt + qt) * nkt + kc + kl] = (uint8_t)v;
+      nf += v == PBA_TILE_FULL;
+      np += v == PBA_TILE_PARTIAL;
+      ns += v == PBA_TILE_SKIP;
+    }
+    __syncthreads();
   }
   if (nf) atomicAdd(&cnt[0], nf);
   if (np) atomicAdd(&cnt[1], np);
@@ -286,17 +304,29 @@ __global__ void __launch_bounds__(kOrderThreads) map_order(MapSet ms) {
   auto count_of = [&](int i) { return min(max(cnt[2 * i] + cnt[2 * i + 1], 0), maxc); };
 
   if (n <= kOrderLds) {
-    for (int i = tid; i < n; i += kOrderThreads) s_c[i] = count_of(i);
+    // Bitonic sort in LDS of the unique keys (maxc - count) * 2^11 + index
+    // (count descending, index ascending; maxc < 2^19 and n <= 2^11, so the
+    // keys fit in 31 bits), padded to a power of two with the largest int.
+    int n2 = 1;
+    while (n2 < n) n2 <<= 1;
+    for (int i = tid; i < n2; i += kOrderThreads) s_c[i] = i < n ? ((maxc - count_of(i)) << 11) | i : 0x7fffffff;
     __syncthreads();
-    for (int i = tid; i < n; i += kOrderThreads) {
-      const int c = s_c[i];
-      int rank = 0;
-      for (int j = 0; j < n; ++j) {
-        const int x = s_c[j];
-        rank += (x > c || (x == c && j < i)) ? 1 : 0;
+    for (int k = 2; k <= n2; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < n2; i += kOrderThreads) {
+          const int l = i ^ j;
+          if (l > i) {
+            const int a = s_c[i], b = s_c[l];
+            if ((a > b) == ((i & k) == 0)) {
+              s_c[i] = b;
+              s_c[l] = a;
+            }
+          }
+        }
+        __syncthreads();
       }
-      order[rank] = i;
     }
+    for (int i = tid; i < n; i += kOrderThreads) order[i] = s_c[i] & 2047;
     return;
   }
 
