@@ -117,11 +117,19 @@ def _sample_rows(rng, pk_b, n):
     return np.sort(pick)
 
 
-@pytest.mark.parametrize("cfg,unscaled", [(2, False), (2, True), (3, False), (4, False), (5, False),
-                                          (3, True), (4, True), (5, True), ("3alt", False)])
-def test_full_size_sampled(cfg, unscaled):
-    w = make_workload(cfg, 0, unscaled=unscaled)
-    say("parity full-size", cfg, "unscaled" if unscaled else "scaled", w.packset.B, w.packset.S)
+@pytest.mark.parametrize("seed", [1, 2])
+def test_tiny_config_other_seeds(seed):
+    say("parity tiny seed", seed)
+    w = make_workload(1, seed)
+    _check_full(w, run_fwd_bwd(w), f"tiny seed {seed}")
+
+
+@pytest.mark.parametrize("cfg,unscaled,seed", [(2, False, 0), (2, True, 0), (3, False, 0), (4, False, 0), (5, False, 0),
+                                               (3, True, 0), (4, True, 0), (5, True, 0), ("3alt", False, 0),
+                                               (2, False, 1), (2, False, 2)])
+def test_full_size_sampled(cfg, unscaled, seed):
+    w = make_workload(cfg, seed, unscaled=unscaled)
+    say("parity full-size", cfg, "unscaled" if unscaled else "scaled", "seed", seed, w.packset.B, w.packset.S)
     got = run_fwd_bwd(w)
     P, R = descriptor_arrays(w.packset)
     pk, br, _ = oracle.token_ids(P, R, w.packset.B, w.packset.S)
