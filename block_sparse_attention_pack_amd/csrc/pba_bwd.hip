@@ -289,48 +289,77 @@ __device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D
                                           const float* __restrict__ sd, int q0, float scale_log2, int qrel, int qlim,
                                           int lane) {
   using C = BwdCfg<D>;
+  // Hand-scheduled: the S / dP MFMAs (A = Q / dO rows, B = K / V rows, both
+  // from LDS), the vector work of query rows 0-15 of the 32 (registers 0-7),
+  // then the dV / dK MFMAs of those rows with the vector work of rows 16-31
+  // between them, then the dV / dK MFMAs of rows 16-31.  Operand reads run
+  // two MFMAs ahead.
+  constexpr int NSD = 2 * C::NS, NG = 2 * C::NE, N = NSD + 2 * NG;
   const int l32 = lane & 31, hi = lane >> 5;
+  struct Ops {
+    bf16x8 a, b;
+  };
+  auto operand = [&](int i) __attribute__((always_inline)) -> Ops {
+    if (i < NSD) {  // S (even) / dP (odd), k-step i / 2
+      const int st = i >> 1;
+      const int qo = prow(q0 + l32) * C::STR + 16 * st + 8 * hi;
+      const int ko = prow(k0 + l32) * C::STR + 16 * st + 8 * hi;
+      return (i & 1) ? Ops{*(const bf16x8*)(sdo + qo), *(const bf16x8*)(sv + ko)}
+                     : Ops{*(const bf16x8*)(sq + qo), *(const bf16x8*)(sk + ko)};
+    }
+    const int k = i - NSD, u = k / NG, e = (k % NG) >> 1;  // dV (even) / dK (odd) of row half u
+    const int r0 = q0 + 16 * u + 4 * hi;
+    return Ops{lds_tr8p((k & 1) ? sq : sdo, C::STR, r0, r0 + 8, 32 * e, lane), bf16x8{}};
+  };
   f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-  for (int st = 0; st < C::NS; ++st) {
-    const bf16x8 qa = *(const bf16x8*)(sq + prow(q0 + l32) * C::STR + 16 * st + 8 * hi);
-    const bf16x8 kb = *(const bf16x8*)(sk + prow(k0 + l32) * C::STR + 16 * st + 8 * hi);
-    s = mfma32(qa, kb, s);
-    const bf16x8 da = *(const bf16x8*)(sdo + prow(q0 + l32) * C::STR + 16 * st + 8 * hi);
-    const bf16x8 vb = *(const bf16x8*)(sv + prow(k0 + l32) * C::STR + 16 * st + 8 * hi);
-    dp = mfma32(da, vb, dp);
-  }
+  f32x4 lv[4], dv[4];
+  bf16x8 pb[2], db[2];
+  // Score r (register r: query row q0 + 8*(r/4) + 4*hi + r%4).
+  auto score = [&](int r) __attribute__((always_inline)) {
+    const int rg = r >> 2, t = r & 3;
+    const int qr = q0 + 8 * rg + 4 * hi + t;
+    float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -lv[rg][t]));
+    p = (unsigned)(qr - qrel) < (unsigned)qlim ? p : 0.f;
+    s[r] = p;
+    dp[r] = p * (dp[r] - dv[rg][t]);
+  };
+  Ops ops[3];
+  ops[0] = operand(0);
+  ops[1] = operand(1);
   sched_fence();
+  static_for<0, N>([&](auto ic) __attribute__((always_inline)) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i + 2 < N) ops[(i + 2) % 3] = operand(i + 2);
+    if constexpr (i < NSD) {
+      if constexpr (i & 1) dp = mfma32(ops[i % 3].a, ops[i % 3].b, dp);
+      else s = mfma32(ops[i % 3].a, ops[i % 3].b, s);
+      if constexpr (i < 4) {  // LSE2 / Delta of the four row groups
+        const int qr = q0 + 8 * i + 4 * hi;
+        lv[i] = *(const f32x4*)(sl + qr);
+        dv[i] = *(const f32x4*)(sd + qr);
+      }
+      if constexpr (i == NSD - 1) {
+        sched_fence();
 #pragma unroll
-  for (int rg = 0; rg < 4; ++rg) {
-    const int qr = q0 + 8 * rg + 4 * hi;  // rows qr .. qr+3 in registers 4*rg .. 4*rg+3
-    const f32x4 lv = *(const f32x4*)(sl + qr);
-    const f32x4 dv = *(const f32x4*)(sd + qr);
+        for (int r = 0; r < 8; ++r) score(r);
+        pb[0] = pack8(s, 0);
+        db[0] = pack8(dp, 0);
+      }
+    } else {
+      constexpr int k = i - NSD, u = k / NG, e = (k % NG) >> 1;
+      if constexpr (k & 1) dkt[e] = mfma32(ops[i % 3].a, db[u], dkt[e]);
+      else dvt[e] = mfma32(ops[i % 3].a, pb[u], dvt[e]);
+      if constexpr (u == 0) {  // rows 16-31 (registers 8-15) spread over these NG MFMAs
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int r = 4 * rg + t;
-      float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -lv[t]));
-      p = (unsigned)(qr + t - qrel) < (unsigned)qlim ? p : 0.f;
-      s[r] = p;
-      dp[r] = p * (dp[r] - dv[t]);
+        for (int r = 8 + 8 * k / NG; r < 8 + 8 * (k + 1) / NG; ++r) score(r);
+        if constexpr (k == NG - 1) {
+          pb[1] = pack8(s, 8);
+          db[1] = pack8(dp, 8);
+        }
+      }
     }
-  }
-  const bf16x8 pb[2] = {pack8(s, 0), pack8(s, 8)};
-  const bf16x8 db[2] = {pack8(dp, 0), pack8(dp, 8)};
-  sched_fence();
-  // dV^T += dO^T P and dK^T += Q^T dS (reduction over the 32 queries, in
-  // the register order of P / dS).
-#pragma unroll
-  for (int e = 0; e < C::NE; ++e) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int r0 = q0 + 16 * u + 4 * hi;
-      const bf16x8 doT = lds_tr8p(sdo, C::STR, r0, r0 + 8, 32 * e, lane);
-      dvt[e] = mfma32(doT, pb[u], dvt[e]);
-      const bf16x8 qT = lds_tr8p(sq, C::STR, r0, r0 + 8, 32 * e, lane);
-      dkt[e] = mfma32(qT, db[u], dkt[e]);
-    }
-  }
+    sched_fence();
+  });
 }
 
 // End of bwd_dkdv: the wave of query half 1 puts its partial sums in its
