@@ -364,10 +364,12 @@ __device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D
 
 // End of bwd_dkdv: the wave of query half 1 puts its partial sums in its
 // lane-private LDS slot, the partner wave (half 0) adds them to its own and
-// writes scale * sum as bf16 (lane: head dims 32e + 8*(r/4) + 4*hi + r%4).
-template <int D>
-__device__ __forceinline__ void pair_sum_store(const f32x16 (&acc)[D / 32], float* slot, int qh, bool valid,
-                                               bf16* out, float scale) {
+// writes scale * sum as bf16 into the row block `rows` (LDS, row = the
+// lane's key within the workgroup, LSTR bytes apart; lane: head dims
+// 32e + 8*(r/4) + 4*hi + r%4), from which the workgroup stores whole rows.
+template <int D, int LSTR>
+__device__ __forceinline__ void pair_sum_lds(const f32x16 (&acc)[D / 32], float* slot, int qh, char* rows, int krow,
+                                             int hi, float scale) {
   constexpr int NE = D / 32;
   if (qh == 1) {
 #pragma unroll
@@ -378,7 +380,8 @@ __device__ __forceinline__ void pair_sum_store(const f32x16 (&acc)[D / 32], floa
             f32x4{acc[e][4 * rg], acc[e][4 * rg + 1], acc[e][4 * rg + 2], acc[e][4 * rg + 3]};
   }
   __syncthreads();
-  if (qh == 0 && valid) {
+  if (qh == 0) {
+    char* row = rows + krow * LSTR + 8 * hi;
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
 #pragma unroll
@@ -387,7 +390,7 @@ __device__ __forceinline__ void pair_sum_store(const f32x16 (&acc)[D / 32], floa
         bf16x4 v;
 #pragma unroll
         for (int t = 0; t < 4; ++t) v[t] = (bf16)((acc[e][4 * rg + t] + o[t]) * scale);
-        *(bf16x4*)(out + 32 * e + 8 * rg) = v;
+        *(bf16x4*)(row + 2 * (32 * e + 8 * rg)) = v;
       }
     }
   }
@@ -411,7 +414,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   // blocks 0-1 in sQ, 2-3 in sDO (2 waves x 64 lanes x D/2 fp32 each).
   __shared__ __attribute__((aligned(1024))) bf16 sQ[2][TQ];
   __shared__ __attribute__((aligned(1024))) bf16 sDO[2][TQ];
-  static_assert(2 * TQ * sizeof(bf16) >= 2 * 64 * (D / 2) * sizeof(float), "exchange must fit a staging array");
+  static_assert(2 * TQ * sizeof(bf16) >= 2 * 64 * (D / 2 + 4) * sizeof(float), "exchange must fit a staging array");
   __shared__ __attribute__((aligned(16))) float sL[2][64], sD[2][64];
 
   const MapView& mp = a.kmap;
@@ -492,10 +495,19 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   // 32e + 8*(r/4) + 4*hi + r%4.
   float* xch = reinterpret_cast<float*>(kb < 2 ? &sQ[0][0] : &sDO[0][0]);
   const int hi = lane >> 5;
-  const int64_t off = (((int64_t)b * S + min(kj, S - 1)) * Hkv + g) * D + 4 * hi;
-  float* slot = xch + ((kb & 1) * 64 + lane) * (D / 2);
-  pair_sum_store<D>(dkt, slot, qh, kj < S, a.dk + off, a.scale);
-  pair_sum_store<D>(dvt, slot, qh, kj < S, a.dv + off, 1.f);
+  // Slots D/2 + 4 floats apart: 16 consecutive lanes start on 16 distinct
+  // 4-bank groups, so the 16-byte slot reads and writes are conflict-free.
+  float* slot = xch + ((kb & 1) * 64 + lane) * (D / 2 + 4);
+  // The summed dK and dV blocks (128 keys x D) go to the resident K / V
+  // areas, free after the loop, and leave as whole rows.
+  using Blk = RowBlock<128, D * 2>;
+  static_assert(128 * Blk::LSTR <= 128 * C::STR * 2, "a dK / dV block fits the K / V area");
+  pair_sum_lds<D, Blk::LSTR>(dkt, slot, qh, (char*)sK, 32 * kb + l32, hi, a.scale);
+  pair_sum_lds<D, Blk::LSTR>(dvt, slot, qh, (char*)sV, 32 * kb + l32, hi, 1.f);
+  const int krows = min(128, S - kt * 128);
+  const int64_t out = ((int64_t)b * S + kt * 128) * kvstride + (int64_t)g * D;
+  Blk::template store<512>(a.dk + out, (const char*)sK, krows, kvstride * 2, tid);
+  Blk::template store<512>(a.dv + out, (const char*)sV, krows, kvstride * 2, tid);
 }
 
 template <int D>
