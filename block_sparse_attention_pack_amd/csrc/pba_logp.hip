@@ -12,8 +12,8 @@
 //               16 bytes per lane per load, four loads in flight) through an
 //               online log-sum-exp in the log2 domain, fp32; bound by HBM
 //               (2 bytes per logit read once)
-//   resp_logp   one wave per pack: each response's sum with a fixed reduction
-//               order (deterministic)
+//   resp_logp   one workgroup per pack: each response's sum with a fixed
+//               reduction order (deterministic)
 #include "pba_next.h"
 #include "pba_tile.h"
 
@@ -112,21 +112,32 @@ __global__ void __launch_bounds__(kLpThreads) token_logp(LogpArgs a) {
   }
 }
 
+// One workgroup per pack: each response's terms are summed by all 256
+// threads (thread t takes terms t, t+256, ...), then across lanes and waves
+// in a fixed order, so the result does not depend on timing.
 __global__ void __launch_bounds__(kLpThreads) resp_logp(RespSumArgs a) {
   if (a.status[0] != 0) return;
-  const int p = blockIdx.x * (kLpThreads / 64) + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (p >= a.n_packs) return;
+  const int p = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  __shared__ float part[kLpThreads / 64];
   const pba_pack pk = a.packs[p];
   const int64_t base = (int64_t)pk.row * a.S;
   int rs = pk.start + pk.prompt_len;
   for (int k = 0; k < pk.n_resp; ++k) {
     const int len = a.resp_len[pk.resp_first + k];
     float s = 0.f;
-    for (int i = lane; i < len; i += 64) s += a.tok_logp[base + rs + i];
+    for (int i = tid; i < len; i += kLpThreads) s += a.tok_logp[base + rs + i];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) a.resp_logp[pk.resp_first + k] = s;
+    if (lane == 0) part[w] = s;
+    __syncthreads();
+    if (tid == 0) {
+      float t = part[0];
+#pragma unroll
+      for (int i = 1; i < kLpThreads / 64; ++i) t += part[i];
+      a.resp_logp[pk.resp_first + k] = t;
+    }
+    __syncthreads();
     rs += len;
   }
 }
@@ -136,7 +147,7 @@ __global__ void __launch_bounds__(kLpThreads) resp_logp(RespSumArgs a) {
 hipError_t launch_token_logp(const LogpArgs& a, const RespSumArgs* r, hipStream_t stream) {
   if (a.ntok > 0) token_logp<<<(unsigned)a.ntok, kLpThreads, 0, stream>>>(a);
   if (r && r->n_packs > 0)
-    resp_logp<<<(unsigned)((r->n_packs + kLpThreads / 64 - 1) / (kLpThreads / 64)), kLpThreads, 0, stream>>>(*r);
+    resp_logp<<<(unsigned)r->n_packs, kLpThreads, 0, stream>>>(*r);
   return hipGetLastError();
 }
 
