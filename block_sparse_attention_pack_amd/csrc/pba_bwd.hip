@@ -9,15 +9,19 @@
 //
 //   bwd_dq    query-major, on the map of the forward's tile shape.  A
 //             workgroup = one query tile x WGH q heads of one kv group, one
-//             wave = 32 queries of one head.  It forms Delta from dO and O in
-//             registers and writes Delta and the log2-domain LSE (0 where the
-//             row sees nothing) for bwd_dkdv, then walks the query tile's key
-//             tiles: S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
+//             wave = 32 queries of one head.  Its prologue stages the Q and
+//             dO blocks, then the O block with the first K/V tile, forms
+//             Delta = rowsum(dO * O) and writes Delta and the log2-domain LSE
+//             (0 where the row sees nothing) for bwd_dkdv; then it walks the
+//             query tile's key tiles: S^T = K Q^T, dP^T = V dO^T, dS^T,
+//             dQ^T += K^T dS^T, the two 32-key halves of a tile staggered.
 //   bwd_dkdv  key-major, on a map with 64-query x 128-key tiles.  A
-//             workgroup = one key tile x one kv group, one wave = 32 keys whose
-//             K and V stay in registers.  It walks the key tile's query tiles
-//             and, for each q head of the group, S = Q K^T, dP = dO V^T,
-//             dV^T += dO^T P, dK^T += Q^T dS, summing over the group's heads.
+//             workgroup = one key tile x one kv group, 8 waves (32 keys x one
+//             32-query half each); K and V of the 128 keys stay in LDS, a
+//             wave's dK^T / dV^T in registers.  It walks the key tile's query
+//             tiles and, for each q head of the group, S = Q K^T, dP = dO V^T,
+//             dV^T += dO^T P, dK^T += Q^T dS, summing over the group's heads;
+//             the two query halves' partial sums meet in LDS at the end.
 //
 // dQ and dK / dV are each owned by exactly one workgroup, so they are written
 // once, in bf16, with no accumulator pass (fp32 atomics into a dQ buffer are

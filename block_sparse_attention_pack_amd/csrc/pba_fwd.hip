@@ -11,11 +11,14 @@
 // and WGH q heads that share a kv head (grouped-query attention); each wave
 // owns 32 query rows of one q head.  Workgroups are launched in the map's
 // longest-list-first order, and consecutive workgroups take different head
-// groups of the same query tile.  K and V tiles of 64 keys are staged in
-// LDS once per workgroup with direct global-to-LDS loads (double-buffered,
-// the next tile's loads in flight during this tile's math, one barrier per
-// tile) and read by all of its waves.  Two workgroups share a compute unit, so one wave's
-// softmax (vector ALU) overlaps the other's MFMAs.
+// groups of the same query tile.  The Q block and the K and V tiles of 64
+// keys are staged in LDS once per workgroup with direct global-to-LDS loads
+// and read by all of its waves.  The key tiles are software-pipelined: a
+// step runs P V of tile j-1, the softmax of tile j and the scores of tile
+// j+1 (hand-scheduled so that MFMAs and the softmax's vector work alternate
+// within a wave), with K loaded two steps ahead and V one step ahead and one
+// barrier per step.  Two workgroups share a compute unit, so each SIMD also
+// interleaves two waves.
 //
 // Scores are computed transposed, S^T = K Q^T (keys on MFMA rows, queries on
 // MFMA columns), so each lane owns a whole query column: the softmax row max

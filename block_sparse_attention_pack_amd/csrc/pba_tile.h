@@ -121,8 +121,6 @@ struct Stager {
   static constexpr int NI = ROWS * STR * 2 / 1024;  // 1 KB instructions per tile
   static constexpr int PER_WAVE = (NI + NWAVES - 1) / NWAVES;
   static_assert((ROWS * STR * 2) % 1024 == 0, "tile must be whole 1 KB blocks");
-  // DMA instructions that wave w issues per stage() call.
-  static constexpr int issued(int w) { return NI - w * PER_WAVE < 0 ? 0 : (NI - w * PER_WAVE < PER_WAVE ? NI - w * PER_WAVE : PER_WAVE); }
   int off[PER_WAVE];  // byte offset of this lane's chunk from the tile's first row
   int w;
   int row_stride;
@@ -151,41 +149,6 @@ struct Stager {
       if (q < NI) dma_to_lds<16>(rs, lds_tile + 512 * q, off[i]);
     }
 #endif
-  }
-};
-
-// Register staging of 64 rows x D (256 threads): thread tid holds the
-// 16-byte chunks tid + 256*i, i < CH, of the tile in row-major chunk order;
-// stored with row r at LDS row prow(r).
-// Loads go through a buffer resource whose range ends at the last valid row
-// (rows past it read as zero); the per-lane offsets are fixed, the tile's
-// position is in the (scalar) resource.
-template <int D, int STR>
-struct RegStager {
-  static constexpr int CH = 64 * D / 8 / 256;
-  int off[CH];  // byte offset of chunk i from the tile's first row
-  int row_stride;
-
-  __device__ __forceinline__ RegStager(int tid, int row_stride_elems) : row_stride(row_stride_elems) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + 256 * i;
-      off[i] = (c / (D / 8)) * row_stride_elems * 2 + 16 * (c % (D / 8));
-    }
-  }
-  __device__ __forceinline__ void load(u32x4 (&r)[CH], const bf16* tile, int rows) const {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const __amdgpu_buffer_rsrc_t rs = rows_rsrc(tile, rows, row_stride, D);
-#pragma unroll
-    for (int i = 0; i < CH; ++i) r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], 0, 0));
-#endif
-  }
-  __device__ __forceinline__ static void store(bf16* lds_tile, const u32x4 (&r)[CH], int tid) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + 256 * i;
-      *(u32x4*)(lds_tile + prow(c / (D / 8)) * STR + 8 * (c % (D / 8))) = r[i];
-    }
   }
 };
 
@@ -253,26 +216,6 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
-
-// Waits until at most `keep` (wave-uniform, 0..15) vector memory
-// operations of this wave are outstanding: the older ones have completed,
-// the `keep` most recent may still be in flight (the counter retires in
-// issue order).  Other counters are not waited for.
-__device__ __forceinline__ void wait_vmem_keep(int keep) {
-#define PBA_WAIT_CASE(N) \
-  case N:                \
-    __builtin_amdgcn_s_waitcnt((N) | (7 << 4) | (15 << 8)); \
-    break;
-  switch (keep) {
-    PBA_WAIT_CASE(1) PBA_WAIT_CASE(2) PBA_WAIT_CASE(3) PBA_WAIT_CASE(4) PBA_WAIT_CASE(5) PBA_WAIT_CASE(6)
-    PBA_WAIT_CASE(7) PBA_WAIT_CASE(8) PBA_WAIT_CASE(9) PBA_WAIT_CASE(10) PBA_WAIT_CASE(11) PBA_WAIT_CASE(12)
-    PBA_WAIT_CASE(13) PBA_WAIT_CASE(14) PBA_WAIT_CASE(15)
-    default:
-      __builtin_amdgcn_s_waitcnt(0);
-      break;
-  }
-#undef PBA_WAIT_CASE
-}
 
 // Keeps the instruction scheduler from moving anything across this point
 // (used between the phases of a tile so that operand loads of a later
