@@ -20,6 +20,8 @@ method equals ordinary masked softmax attention):
                          response loss mask from descriptors
   logprob.token_logp / response_logp   log-softmax at the gather rows and
                          per-response sums
+  groupdpo               group preference objectives over packs of K
+                         responses and their surrogate coefficients
 
 Every function is pinned in tests/ against facts the pages or mathematics
 fix (worked masks, closed-form counts, brute force, finite differences,
@@ -33,3 +35,4 @@ from .attention import (  # noqa: F401
 )
 from .positions import positions  # noqa: F401
 from .logprob import row_logsumexp, token_logp, response_logp  # noqa: F401
+from . import groupdpo  # noqa: F401
