@@ -27,7 +27,7 @@ TILE_SKIP, TILE_PARTIAL, TILE_FULL = 0, 1, 2
 EXPORTED = ("pba_strerror", "pba_fwd_tile", "pba_bwd_tile", "pba_map_bytes", "pba_map_init",
             "pba_pack_block_map", "pba_pack_block_maps", "pba_packed_attn_fwd", "pba_bwd_workspace_bytes", "pba_packed_attn_bwd",
             "pba_packed_attn_bwd_stages", "pba_mfma_probe", "pba_pack_positions",
-            "pba_packed_token_logp")
+            "pba_packed_token_logp", "pba_group_coefficients")
 
 
 class PbaBlockMap(ctypes.Structure):
@@ -75,6 +75,11 @@ _lib.pba_packed_token_logp.argtypes = [ctypes.POINTER(PbaBlockMap), ctypes.c_voi
                                        ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
 _lib.pba_packed_token_logp.restype = ctypes.c_int
+_lib.pba_group_coefficients.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+_lib.pba_group_coefficients.restype = ctypes.c_int
 _lib.pba_mfma_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
 _lib.pba_mfma_probe.restype = ctypes.c_int
 BWD_DQ, BWD_DKDV, BWD_ALL = 1, 2, 3
@@ -333,3 +338,51 @@ def packed_token_logp(m: BlockMap, src_row, loss_mask, logits, tokens, packs_dev
                                       tokens.data_ptr(), tok.data_ptr(), ptr(resp), _stream(stream)),
            "pba_packed_token_logp")
     return tok, resp
+
+
+GROUP_OBJECTIVES = {"all_pairs": 0, "margin": 1, "mpo": 2, "softmax": 3}
+GROUP_MAX_ENTRIES = 4096
+
+
+def groups_from_packs(n_resp_per_pack, positive):
+    """CSR group arrays (group_ptr, member) with one group per pack, whose
+    entries are that pack's responses in order; `positive` (one flag per
+    response, packs in order) marks the preferred ones.  Host-side index
+    bookkeeping only."""
+    n = [int(x) for x in n_resp_per_pack]
+    ptr = [0]
+    for x in n:
+        ptr.append(ptr[-1] + x)
+    if len(positive) != ptr[-1]:
+        raise ValueError("one positive flag per response")
+    return (torch.tensor(ptr, dtype=torch.int32), torch.arange(ptr[-1], dtype=torch.int32),
+            torch.as_tensor(positive, dtype=torch.uint8))
+
+
+def group_coefficients(group_ptr, member, positive, pol, ref, resp_len, beta: float, objective="all_pairs",
+                       alpha: float = 1.0, out=None, stream=None):
+    """(coef fp32 [n_resp], nll_w fp32 [n_resp], loss fp32 [2], status int32
+    [2]): surrogate coefficients of a group preference objective, the
+    positive-NLL weights, (L_group, NLL term) and the device status, from
+    device arrays (group_ptr int32 [G+1], member int32 / positive uint8
+    [E], pol / ref fp32 and resp_len int32 [n_resp])."""
+    obj = GROUP_OBJECTIVES[objective] if isinstance(objective, str) else int(objective)
+    for t, dt in ((group_ptr, torch.int32), (member, torch.int32), (positive, torch.uint8), (pol, torch.float32),
+                  (ref, torch.float32), (resp_len, torch.int32)):
+        if t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"expected a contiguous {dt} tensor")
+    n_resp = pol.numel()
+    if ref.numel() != n_resp or resp_len.numel() != n_resp or positive.numel() != member.numel():
+        raise ValueError("array sizes do not match")
+    if out is None:
+        dev = pol.device
+        out = (torch.empty(n_resp, dtype=torch.float32, device=dev), torch.empty(n_resp, dtype=torch.float32, device=dev),
+               torch.empty(2, dtype=torch.float32, device=dev), torch.empty(2, dtype=torch.int32, device=dev))
+    coef, nll_w, loss, status = out
+    ptr = lambda x: None if x is None else x.data_ptr()  # noqa: E731
+    _check(_lib.pba_group_coefficients(group_ptr.data_ptr(), group_ptr.numel() - 1, member.data_ptr(),
+                                       positive.data_ptr(), member.numel(), pol.data_ptr(), ref.data_ptr(),
+                                       resp_len.data_ptr(), n_resp, obj, float(beta), float(alpha), coef.data_ptr(),
+                                       ptr(nll_w), ptr(loss), status.data_ptr(), _stream(stream)),
+           "pba_group_coefficients")
+    return coef, nll_w, loss, status

@@ -3,6 +3,7 @@
 // stream.  Descriptor contents are checked on the device by the map kernels.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstring>
 #include <mutex>
 
@@ -130,11 +131,17 @@ const char* pba_strerror(int code) {
     case PBA_ERR_DEVICE: return "no gfx950 device current, or a HIP launch failed";
     case PBA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
     case PBA_ERR_SCALE: return "softmax scale must be positive and finite";
+    case PBA_ERR_ARG: return "objective unknown, or beta / alpha out of range";
     case PBA_DESC_ROW: return "descriptor: row outside [0, B)";
     case PBA_DESC_NEGATIVE: return "descriptor: negative start, length or response count";
     case PBA_DESC_RESP_RANGE: return "descriptor: response range outside resp_len";
     case PBA_DESC_BOUNDS: return "descriptor: pack runs past the end of its row";
     case PBA_DESC_ORDER: return "descriptor: packs not sorted by (row, start) or overlapping";
+    case PBA_GROUP_BAD_PTR: return "groups: group_ptr not non-decreasing from 0 to n_entries";
+    case PBA_GROUP_BAD_MEMBER: return "groups: member outside [0, n_resp)";
+    case PBA_GROUP_BAD_LENGTH: return "groups: member response length not positive";
+    case PBA_GROUP_DUPLICATE: return "groups: response named twice in one group";
+    case PBA_GROUP_EMPTY_SET: return "groups: group without a positive or without a negative";
     default: return "unknown code";
   }
 }
@@ -271,6 +278,36 @@ int pba_packed_token_logp(const pba_block_map* map, const pba_pack* packs, int n
   return pba::launch_token_logp(a, resp_logp ? &r : nullptr, static_cast<hipStream_t>(stream)) == hipSuccess
              ? PBA_OK
              : PBA_ERR_DEVICE;
+}
+
+int pba_group_coefficients(const int32_t* group_ptr, int n_groups, const int32_t* member, const uint8_t* positive,
+                           int n_entries, const float* pol, const float* ref, const int32_t* resp_len, int n_resp,
+                           int objective, float beta, float alpha, float* coef, float* nll_w, float* loss,
+                           int32_t* status, void* stream) {
+  if (!group_ptr || !member || !positive || !pol || !ref || !resp_len || !coef || !status) return PBA_ERR_NULL;
+  if (n_entries < 2 || n_entries > PBA_GROUP_MAX_ENTRIES || n_groups < 1 || n_groups > n_entries / 2 || n_resp < 1)
+    return PBA_ERR_SHAPE;
+  if (objective < PBA_GROUP_ALL_PAIRS || objective > PBA_GROUP_SOFTMAX) return PBA_ERR_ARG;
+  if (!(beta > 0.f) || !std::isfinite(beta) || !(alpha >= 0.f) || !std::isfinite(alpha)) return PBA_ERR_ARG;
+  if (int rc = device_ok()) return rc;
+  pba::GroupArgs a;
+  a.group_ptr = group_ptr;
+  a.member = member;
+  a.positive = positive;
+  a.pol = pol;
+  a.ref = ref;
+  a.resp_len = resp_len;
+  a.n_groups = n_groups;
+  a.n_entries = n_entries;
+  a.n_resp = n_resp;
+  a.objective = objective;
+  a.beta = beta;
+  a.alpha = alpha;
+  a.coef = coef;
+  a.nll_w = nll_w;
+  a.loss = loss;
+  a.status = status;
+  return pba::launch_group_coef(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PBA_OK : PBA_ERR_DEVICE;
 }
 
 int pba_pack_block_map(const pba_pack* packs, int n_packs, const int32_t* resp_len, int n_resp_total,

@@ -1,5 +1,6 @@
 // Declarations shared by the kernels of the rows that follow attention
-// (positions and log-prob gathering) and the C-ABI layer.
+// (positions, log-prob gathering, group preference coefficients) and the
+// C-ABI layer.
 #pragma once
 
 #include "pba_internal.h"
@@ -38,5 +39,34 @@ struct RespSumArgs {  // resp_logp
   float* resp_logp;
 };
 hipError_t launch_token_logp(const LogpArgs& a, const RespSumArgs* r, hipStream_t stream);
+
+constexpr int kMaxGroupEntries = PBA_GROUP_MAX_ENTRIES;
+constexpr int kMaxGroups = PBA_GROUP_MAX_ENTRIES / 2;  // every group has at least two entries
+enum : int {
+  kObjAllPairs = PBA_GROUP_ALL_PAIRS,
+  kObjMargin = PBA_GROUP_MARGIN,
+  kObjMpo = PBA_GROUP_MPO,
+  kObjSoftmax = PBA_GROUP_SOFTMAX,
+  kGroupPtr = PBA_GROUP_BAD_PTR,
+  kGroupMember = PBA_GROUP_BAD_MEMBER,
+  kGroupLength = PBA_GROUP_BAD_LENGTH,
+  kGroupDuplicate = PBA_GROUP_DUPLICATE,
+  kGroupEmpty = PBA_GROUP_EMPTY_SET,
+};
+struct GroupArgs {  // group_coef
+  const int32_t* group_ptr;
+  const int32_t* member;
+  const uint8_t* positive;
+  const float* pol;
+  const float* ref;
+  const int32_t* resp_len;
+  int n_groups, n_entries, n_resp, objective;
+  double beta, alpha;
+  float* coef;
+  float* nll_w;
+  float* loss;
+  int32_t* status;
+};
+hipError_t launch_group_coef(const GroupArgs& a, hipStream_t stream);
 
 }  // namespace pba

@@ -22,6 +22,10 @@
  *                        class (skip / partial / full) and visit lists
  *   pba_packed_attn_fwd  Q, K, V (bf16, grouped heads) -> O (bf16), LSE (fp32)
  *   pba_packed_attn_bwd  dO -> dQ, dK, dV (bf16)
+ * and the steps around them in a preference-training step: aligned
+ * position ids and log-prob gather rows (pba_pack_positions), packed token
+ * log-probs (pba_packed_token_logp) and group preference coefficients
+ * (pba_group_coefficients).
  *
  * Conventions shared by every call.
  *   - Every array argument is DEVICE memory allocated by the caller.  The
@@ -70,6 +74,7 @@ extern "C" {
 #define PBA_ERR_DEVICE     -8  /* no gfx950 device current, or a HIP launch failed  */
 #define PBA_ERR_ALIGN      -9  /* a tensor pointer is not 16-byte aligned          */
 #define PBA_ERR_SCALE     -10  /* softmax_scale not positive and finite            */
+#define PBA_ERR_ARG       -11  /* objective, beta or alpha out of range            */
 
 /* ---- device status codes (map->status[0]; status[1] = first bad pack) -- */
 #define PBA_DESC_OK          0
@@ -78,6 +83,13 @@ extern "C" {
 #define PBA_DESC_RESP_RANGE  3  /* resp_first / n_resp outside resp_len[]              */
 #define PBA_DESC_BOUNDS      4  /* pack runs past the end of its row                   */
 #define PBA_DESC_ORDER       5  /* packs not sorted by (row, start), or overlapping    */
+
+/* ---- group status codes (pba_group_coefficients; status[1] = first bad group) */
+#define PBA_GROUP_BAD_PTR     11  /* group_ptr not non-decreasing from 0 to n_entries   */
+#define PBA_GROUP_BAD_MEMBER  12  /* member outside [0, n_resp)                         */
+#define PBA_GROUP_BAD_LENGTH  13  /* member's response length not positive              */
+#define PBA_GROUP_DUPLICATE   14  /* response twice in one group (or both signs)        */
+#define PBA_GROUP_EMPTY_SET   15  /* group without a positive or without a negative     */
 
 /* ---- tile classes in map->cls ------------------------------------------ */
 #define PBA_TILE_SKIP     0
@@ -220,6 +232,50 @@ PBA_API int pba_packed_token_logp(const pba_block_map* map, const pba_pack* pack
                                   const int32_t* resp_len, int n_resp_total, const int32_t* src_row,
                                   const uint8_t* loss_mask, const void* logits, int V, const int32_t* tokens,
                                   float* tok_logp, float* resp_logp, void* stream);
+
+/* Group preference objectives and their surrogate coefficients ("GroupDPO"
+ * page, section "core formulas").  A batch holds n_groups groups in CSR
+ * form: group g owns entries [group_ptr[g], group_ptr[g+1]); entry e names
+ * response member[e] and is a positive (positive[e] != 0) or a negative.
+ * Each group needs at least one of each and names a response at most once;
+ * a response may belong to several groups.  From the per-response log-prob
+ * sums of the policy and of the frozen reference (pol, ref: fp32 [n_resp],
+ * e.g. resp_logp of pba_packed_token_logp) and the response lengths
+ * (resp_len, int32 [n_resp], the same array as for the map build):
+ *   u_i      = beta (pol_i / len_i - ref_i / len_i)
+ *   loss[0]  = L_group = (1/n_groups) sum_g phi_g(u[P_g], u[N_g])
+ *   coef[i]  = (1/n_groups) sum_{g containing i} d phi_g / d u_i
+ *              (L_sur = sum_i coef_i u_i has the first-order gradient of
+ *              L_group at this point; 0 for a response in no group)
+ *   nll_w[i] = alpha sum_{g: i in P_g} 1 / (n_groups |P_g|), the weight of
+ *              response i's mean token NLL in the positive-NLL term
+ *   loss[1]  = alpha (1/n_groups) sum_g mean_{i in P_g} (-pol_i / len_i)
+ * where phi is selected by `objective` (each is -log sigmoid(u+ - u-) for
+ * one positive and one negative):
+ *   PBA_GROUP_ALL_PAIRS  mean over (i in P, j in N) of -log sigmoid(u_i - u_j)
+ *   PBA_GROUP_MARGIN     -log sigmoid(mean_P u - mean_N u)
+ *   PBA_GROUP_MPO        log sum_{P u N} e^u - log sum_P e^u
+ *   PBA_GROUP_SOFTMAX    mean over i in P of log(e^{u_i} + sum_N e^u) - u_i
+ * Computed in fp64 by one workgroup, every sum in a fixed order
+ * (deterministic); outputs rounded to fp32.  All arrays are device memory:
+ * group_ptr int32 [n_groups+1], member int32 / positive uint8 [n_entries],
+ * coef fp32 [n_resp], nll_w fp32 [n_resp] (may be NULL), loss fp32 [2]
+ * (may be NULL), status int32 [2] = {PBA_GROUP_* code or 0, first bad group
+ * or 0}.  Group contents are checked on the device: on a bad group, status
+ * is set and coef, nll_w and loss are filled with NaN.  Limits: 2 <=
+ * n_entries <= PBA_GROUP_MAX_ENTRIES, 1 <= n_groups <= n_entries / 2,
+ * n_resp >= 1.  Returns PBA_OK, PBA_ERR_NULL, PBA_ERR_SHAPE, PBA_ERR_ARG
+ * (objective unknown, beta not positive and finite, alpha negative or not
+ * finite) or PBA_ERR_DEVICE. */
+#define PBA_GROUP_ALL_PAIRS 0
+#define PBA_GROUP_MARGIN    1
+#define PBA_GROUP_MPO       2
+#define PBA_GROUP_SOFTMAX   3
+#define PBA_GROUP_MAX_ENTRIES 4096
+PBA_API int pba_group_coefficients(const int32_t* group_ptr, int n_groups, const int32_t* member,
+                                   const uint8_t* positive, int n_entries, const float* pol, const float* ref,
+                                   const int32_t* resp_len, int n_resp, int objective, float beta, float alpha,
+                                   float* coef, float* nll_w, float* loss, int32_t* status, void* stream);
 
 /* Forward.  For every query token and q head: O = softmax(scale * Q K^T
  * restricted to the allowed keys) V, and LSE = natural log of the sum of

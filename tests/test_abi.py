@@ -101,3 +101,32 @@ def test_positions_and_probe_argument_errors():
     assert lib.pba_mfma_probe(None, 1, 1, None) == -1
     assert lib.pba_mfma_probe(16, 0, 1, None) == -2
     assert lib.pba_mfma_probe(16, 1, 0, None) == -2
+
+
+def test_group_coefficients_argument_errors():
+    import block_sparse_attention_pack_amd as P
+    lib = P.api._lib
+    f = lib.pba_group_coefficients
+    p = 16  # a non-NULL stand-in: every case below fails before any device access
+    ok = dict(gp=p, G=1, mem=p, pos=p, E=2, pol=p, ref=p, rl=p, n=2, obj=0, beta=0.1, alpha=1.0, coef=p, nll=None,
+              loss=None, st=p)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["gp"], a["G"], a["mem"], a["pos"], a["E"], a["pol"], a["ref"], a["rl"], a["n"], a["obj"], a["beta"],
+                 a["alpha"], a["coef"], a["nll"], a["loss"], a["st"], None)
+
+    for k in ("gp", "mem", "pos", "pol", "ref", "rl", "coef", "st"):
+        assert call(**{k: None}) == -1, k
+    assert call(E=1) == -2
+    assert call(E=4097, G=2) == -2
+    assert call(G=0) == -2
+    assert call(G=2, E=3) == -2       # a group needs two entries
+    assert call(n=0) == -2
+    assert call(obj=4) == -11
+    assert call(obj=-1) == -11
+    assert call(beta=0.0) == -11
+    assert call(beta=float("inf")) == -11
+    assert call(alpha=-1.0) == -11
+    assert call(alpha=float("nan")) == -11
+    assert "group" in P.api.strerror(15) and "objective" in P.api.strerror(-11)
