@@ -60,7 +60,7 @@ template <int D, bool MASK>
 __device__ __forceinline__ void dq_tile(f32x16 (&dq)[D / 32], const bf16x8 (&qop)[D / 16],
                                         const bf16x8 (&dop)[D / 16], float l2, float delta,
                                         const bf16* __restrict__ sk, const bf16* __restrict__ sv, float scale_log2,
-                                        int lim, int lo, int pc, int plen, int lane) {
+                                        KeyMask km, int lane) {
   using C = BwdCfg<D>;
   constexpr int NSD = 2 * C::NS;    // S and dP MFMAs of one half
   constexpr int NDQ = 2 * C::NE;    // dQ MFMAs of one half
@@ -79,12 +79,7 @@ __device__ __forceinline__ void dq_tile(f32x16 (&dq)[D / 32], const bf16x8 (&qop
   // dS of score x (0..15) of half aa, in place in s[aa].
   auto dscore = [&](f32x16 (&sa)[2], f32x16 (&pa)[2], int aa, int r) __attribute__((always_inline)) {
     float p = fast_exp2(__builtin_fmaf(sa[aa][r], scale_log2, -l2));
-    if (MASK) {
-      const int off = 32 * aa + 8 * (r >> 2) + (r & 3);
-      // (bitwise, not short-circuit: no branches between the MFMAs)
-      const bool ok = (off <= lim) & ((off >= lo) | ((unsigned)(off + pc) < (unsigned)plen));
-      p = ok ? p : 0.f;
-    }
+    if (MASK) p = keep_or_zero(mask_bit(aa ? km.hi : km.lo, 8 * (r >> 2) + (r & 3)), p);
     sa[aa][r] = p * (pa[aa][r] - delta);
   };
   f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
@@ -237,10 +232,10 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
     }
     if constexpr (decltype(masked)::value) {
       const int jb = kt * 64 + 4 * hi;
-      dq_tile<D, true>(dq, qop, dop, l2, delta, sK(buf), sV(buf), a.scale_log2, qi - jb, wlo - jb, jb - wplo,
-                       wphi - wplo, lane);
+      dq_tile<D, true>(dq, qop, dop, l2, delta, sK(buf), sV(buf), a.scale_log2,
+                       key_mask(qi - jb, wlo - jb, jb - wplo, wphi - wplo), lane);
     } else {
-      dq_tile<D, false>(dq, qop, dop, l2, delta, sK(buf), sV(buf), a.scale_log2, 0, 0, 0, 0, lane);
+      dq_tile<D, false>(dq, qop, dop, l2, delta, sK(buf), sV(buf), a.scale_log2, KeyMask{0u, 0u}, lane);
     }
     wait_vmem();
     __syncthreads();
@@ -282,16 +277,17 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
 // One (query tile, q head) step for one wave of bwd_dkdv: one 32-query half
 // of the 64-query tile (rows q0 .. q0+31 of the staged tiles) x the wave's
 // 32 keys (rows k0 .. k0+31 of the resident K / V tiles).  Query
-// q0 + 8*(r/4) + 4*hi + r%4 sits in register r of s; the lane's key kj is
-// seen by queries [kj, qend): row index x of the tile is visible iff
-// (unsigned)(x - qrel) < (unsigned)qlim (qrel = kj - first query of the tile,
-// qlim = qend - kj; qlim = -1 admits every row).
-template <int D>
+// q0 + 8*(r/4) + 4*hi + r%4 sits in register r of s.  On partial tiles
+// (MASK) the lane's key kj is seen by queries [kj, qend): row index x of the
+// tile is visible iff (unsigned)(x - qrel) < (unsigned)qlim (qrel = kj - the
+// tile's first query, qlim = qend - kj).  These compares depend on the tile
+// only, so the compiler keeps them in scalar lane masks across the q heads.
+template <int D, bool MASK>
 __device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D / 32], const bf16* __restrict__ sk,
                                           const bf16* __restrict__ sv, int k0, const bf16* __restrict__ sq,
                                           const bf16* __restrict__ sdo, const float* __restrict__ sl,
-                                          const float* __restrict__ sd, int q0, float scale_log2, int qrel, int qlim,
-                                          int lane) {
+                                          const float* __restrict__ sd, int q0, float scale_log2, int qrel,
+                                          int qlim, int lane) {
   using C = BwdCfg<D>;
   // Hand-scheduled: the S / dP MFMAs (A = Q / dO rows, B = K / V rows, both
   // from LDS), the vector work of query rows 0-15 of the 32 (registers 0-7),
@@ -321,9 +317,8 @@ __device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D
   // Score r (register r: query row q0 + 8*(r/4) + 4*hi + r%4).
   auto score = [&](int r) __attribute__((always_inline)) {
     const int rg = r >> 2, t = r & 3;
-    const int qr = q0 + 8 * rg + 4 * hi + t;
     float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -lv[rg][t]));
-    p = (unsigned)(qr - qrel) < (unsigned)qlim ? p : 0.f;
+    if (MASK) p = (unsigned)(q0 + 8 * rg + 4 * hi + t - qrel) < (unsigned)qlim ? p : 0.f;
     s[r] = p;
     dp[r] = p * (dp[r] - dv[rg][t]);
   };
@@ -474,24 +469,25 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   wait_vmem();
   __syncthreads();
   int buf = 0;
-  for (int i = 0; i < n; ++i) {
+  // Full query tiles come first in the list, then partial ones; a loop for
+  // each keeps the dK / dV accumulators in place.
+  auto visit = [&](int i, auto masked) {
     const int qt = min(max(list[i], 0), mp.nqt - 1);
-    const bool masked = i >= nfull;
+    const int qrel = kj - qt * 64, qlim = qend - kj;
     for (int hh = 0; hh < G; ++hh) {
       // Prefetch the next step into the other buffer (last read one step ago).
       if (hh + 1 < G) stage(i, hh + 1, buf ^ 1);
       else if (i + 1 < n) stage(i + 1, 0, buf ^ 1);
-      // One code path for full and partial tiles: a full tile gets a
-      // window that admits every query.
-      const int qrel = masked ? kj - qt * 64 : 0;
-      const int qlim = masked ? qend - kj : -1;
-      dkdv_step<D>(dkt, dvt, skp, svp, 32 * kb, sQ[buf], sDO[buf], sL[buf], sD[buf], 32 * qh, a.scale_log2, qrel, qlim,
-                   lane);
+      dkdv_step<D, decltype(masked)::value>(dkt, dvt, skp, svp, 32 * kb, sQ[buf], sDO[buf], sL[buf], sD[buf], 32 * qh,
+                                            a.scale_log2, qrel, qlim, lane);
       wait_vmem();
       __syncthreads();
       buf ^= 1;
     }
-  }
+  };
+  int i = 0;
+  for (; i < nfull; ++i) visit(i, std::false_type{});
+  for (; i < n; ++i) visit(i, std::true_type{});
 
   // Sum the two query halves: the waves of half 1 hand their partial dK^T,
   // then dV^T, to their partners through LDS (lane-private slots in the

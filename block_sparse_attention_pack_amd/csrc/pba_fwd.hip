@@ -94,22 +94,18 @@ __device__ __forceinline__ void fwd_scores(f32x16 (&s)[2], const bf16x8 (&qop)[D
 
 // Online softmax of one tile (masked on partial tiles): updates the running
 // reference m (log2 domain) and sum l, returns the rescale factor alpha of the
-// accumulators and P^T packed as bf16 B operands.  With jb = k0 + 4*hi and
-// o the compile-time part of a key's offset, the key is visible to the
-// lane's query iff o <= lim and (o >= lo or (unsigned)(o + pc) < plen).
+// accumulators and P^T packed as bf16 B operands.  On partial tiles, key
+// jb + o (jb = k0 + 4*hi, o the compile-time part of its register's key
+// offset) is visible to the lane's query iff bit o of km is set.
 template <bool MASK>
 __device__ __forceinline__ void fwd_softmax(f32x16 (&s)[2], float& m, float& l, float& alpha, bf16x8 (&p)[2][2],
-                                            float scale_log2, int lim, int lo, int pc, int plen) {
+                                            float scale_log2, KeyMask km) {
   float mx = kNegInf;
 #pragma unroll
   for (int aa = 0; aa < 2; ++aa) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      if (MASK) {
-        const int off = 32 * aa + 8 * (r >> 2) + (r & 3);
-        const bool ok = off <= lim && (off >= lo || (unsigned)(off + pc) < (unsigned)plen);
-        s[aa][r] = ok ? s[aa][r] : kNegInf;
-      }
+      if (MASK) s[aa][r] = keep_or_ninf(mask_bit(aa ? km.hi : km.lo, 8 * (r >> 2) + (r & 3)), s[aa][r]);
       mx = fmaxf(mx, s[aa][r]);
     }
   }
@@ -139,8 +135,7 @@ __device__ __forceinline__ void fwd_softmax(f32x16 (&s)[2], float& m, float& l, 
 template <int D, bool MASK>
 __device__ __forceinline__ void fwd_step(f32x16 (&o)[D / 32], bf16x8 (&p)[2][2], float& alpha, float& m, float& l,
                                          f32x16 (&s)[2], const bf16x8 (&qop)[D / 16], const bf16* __restrict__ sk,
-                                         const bf16* __restrict__ sv, float scale_log2, int lim, int lo, int pc,
-                                         int plen, int lane) {
+                                         const bf16* __restrict__ sv, float scale_log2, KeyMask km, int lane) {
   using C = FwdCfg<D>;
   constexpr int NPV = C::NE * 4, NQK = C::NS * 2, N = NPV + NQK;
   constexpr int NEXP = NQK - 2;  // score slices of the exp phase (the max arrives after two MFMAs)
@@ -171,12 +166,7 @@ __device__ __forceinline__ void fwd_step(f32x16 (&o)[D / 32], bf16x8 (&p)[2][2],
 #pragma unroll
       for (int x = 32 * i / NPV; x < 32 * (i + 1) / NPV; ++x) {
         const int sa = x >> 4, r = x & 15;
-        if (MASK) {
-          const int off = 32 * sa + 8 * (r >> 2) + (r & 3);
-          // (bitwise, not short-circuit: no branches between the MFMAs)
-          const bool ok = (off <= lim) & ((off >= lo) | ((unsigned)(off + pc) < (unsigned)plen));
-          s[sa][r] = ok ? s[sa][r] : kNegInf;
-        }
+        if (MASK) s[sa][r] = keep_or_ninf(mask_bit(sa ? km.hi : km.lo, 8 * (r >> 2) + (r & 3)), s[sa][r]);
         mx = fmaxf(mx, s[sa][r]);
       }
     } else {
@@ -329,20 +319,14 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
     if (j + 2 < n) kst.stage(sK(j), kb + (int64_t)key0(j + 2) * kvstride, S - key0(j + 2));
     const int jb = key0(j) + 4 * hi;
     constexpr bool MASKED = decltype(masked)::value;
+    const KeyMask km = MASKED ? key_mask(qi - jb, wlo - jb, jb - wplo, wphi - wplo) : KeyMask{0u, 0u};
     if constexpr (decltype(has_prev)::value && decltype(has_next)::value) {
-      if constexpr (MASKED)
-        fwd_step<D, true>(o, p, alpha, m, l, s, qop, sK(j + 1), sV(j - 1), a.scale_log2, qi - jb, wlo - jb,
-                          jb - wplo, wphi - wplo, lane);
-      else
-        fwd_step<D, false>(o, p, alpha, m, l, s, qop, sK(j + 1), sV(j - 1), a.scale_log2, 0, 0, 0, 0, lane);
+      fwd_step<D, MASKED>(o, p, alpha, m, l, s, qop, sK(j + 1), sV(j - 1), a.scale_log2, km, lane);
     } else {
       if constexpr (decltype(has_prev)::value) fwd_pv<D>(o, p, alpha, sV(j - 1), lane);
       f32x16 sn[2];
       if constexpr (decltype(has_next)::value) fwd_scores<D>(sn, qop, sK(j + 1), lane);
-      if constexpr (MASKED)
-        fwd_softmax<true>(s, m, l, alpha, p, a.scale_log2, qi - jb, wlo - jb, jb - wplo, wphi - wplo);
-      else
-        fwd_softmax<false>(s, m, l, alpha, p, a.scale_log2, 0, 0, 0, 0);
+      fwd_softmax<MASKED>(s, m, l, alpha, p, a.scale_log2, km);
       if constexpr (decltype(has_next)::value) {
         s[0] = sn[0];
         s[1] = sn[1];

@@ -47,6 +47,45 @@ __device__ __forceinline__ bf16x8 lds_tr8(const bf16* M, int stride, int r0, int
 // additive in the compile-time parts, so no extra registers are needed.
 __device__ __forceinline__ int prow(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
 
+// Visibility of the 64 keys jb + off (off = 0..63) of a partial tile to one
+// query, as a bit mask (bit off of the pair {lo word, hi word}).  The query
+// sees its pack's shared prompt up to the end of the prompt and its own
+// branch up to itself: with lim = q - jb, the branch run starting at
+// lo = kv_lo - jb and the prompt run [-pc, plen - pc) (pc = jb - pre_lo,
+// plen = pre_hi - pre_lo), key off is visible iff off <= lim and it lies in
+// either run.  Built once per tile; then a score needs one bit extract.
+struct KeyMask {
+  unsigned lo, hi;
+};
+__host__ __device__ __forceinline__ unsigned long long key_run_bits(int a, int b) {
+  // bits [a, b) of 0..63
+  a = a < 0 ? 0 : a;
+  b = b > 64 ? 64 : b;
+  if (b <= a) return 0ull;
+  return (~0ull << a) & (~0ull >> (64 - b));
+}
+__host__ __device__ __forceinline__ KeyMask key_mask(int lim, int lo, int pc, int plen) {
+  const int end = lim + 1;
+  const int pend = plen - pc < end ? plen - pc : end;
+  const unsigned long long m = key_run_bits(lo, end) | key_run_bits(-pc, pend);
+  return {(unsigned)m, (unsigned)(m >> 32)};
+}
+// All ones if bit `bit` (a constant after unrolling) of w is set, else 0
+// (one bit-field extract).
+__device__ __forceinline__ int mask_bit(unsigned w, int bit) { return __builtin_amdgcn_sbfe((int)w, bit, 1); }
+// s where the mask word m is all ones, -inf where it is 0 (one bit-field
+// insert).
+__device__ __forceinline__ float keep_or_ninf(int m, float s) {
+  return __int_as_float((__float_as_int(s) & m) | (int)(0xff800000u & ~(unsigned)m));
+}
+// p where m is all ones, 0 where it is 0.  m is made opaque first: the
+// optimiser would otherwise turn the extract and the AND into a compare and
+// a select (three instructions where two do).
+__device__ __forceinline__ float keep_or_zero(int m, float p) {
+  asm("" : "+v"(m));
+  return __int_as_float(__float_as_int(p) & m);
+}
+
 // lds_tr8 on a tile stored with prow(): r0, r1 are multiples of 4.
 __device__ __forceinline__ bf16x8 lds_tr8p(const bf16* M, int stride, int r0, int r1, int col0, int lane) {
   const int s = lane & 15, G = lane >> 4;
