@@ -240,7 +240,7 @@ def logp_rate(A, torch, r, pos_out, ps, V=151936):
     nbytes = terms * V * 2
     del logits
     return {"vocab": V, "loss_terms": terms, "ms": ms, "hbm_bytes": nbytes,
-            "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+            "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}, resp
 
 
 def cpu_baseline(w, seconds):
@@ -294,6 +294,49 @@ class _RowMask:
     def __getitem__(self, i):
         assert i == self.b
         return self.mb
+
+
+def config_sweep(A, torch, steps, warmup, cfgs=(3, 4, 5)):
+    """The step on the larger workloads (context for the headline one): useful
+    TFLOP/s per workload, each timed like the headline step."""
+    from workloads.generate import make_workload
+    dev = torch.device("cuda:0")
+    out = {}
+    for c in cfgs:
+        w = make_workload(c, 0)
+        t = [x.to(dev).contiguous() for x in (w.q, w.k, w.v, w.do)]
+        r = Runner(A, torch, w.packset, *t, w.Hq, w.Hkv, w.D, w.scale)
+        ms, per = time_runner(torch, r, steps, warmup)
+        useful = 14.0 * w.D * w.Hq * allowed_pairs(w.packset)
+        out[w.name] = {"B": w.packset.B, "S": w.packset.S, "ms_per_step": ms, "useful_tflops": useful / (ms * 1e-3) / 1e12,
+                       "kernels_ms": {k_: round(v_, 4) for k_, v_ in per.items()}}
+        del r, t
+        torch.cuda.empty_cache()
+    return out
+
+
+def group_coef_time(A, torch, r, resp_logp):
+    """pba_group_coefficients on the workload's packs (one group per pack,
+    response 0 preferred), policy and reference sums from the log-prob run."""
+    import numpy as np
+    P = r.P.cpu().numpy().reshape(-1, 5)
+    nresp = [int(x) for x in P[:, 3]]
+    flags = []
+    for k_ in nresp:
+        flags += [1] + [0] * (k_ - 1)
+    gp, mem, pos = (x.cuda() for x in A.groups_from_packs(nresp, flags))
+    ref = resp_logp * 1.01
+    for _ in range(3):
+        out = A.group_coefficients(gp, mem, pos, resp_logp, ref, r.R, 0.1, "all_pairs")
+    torch.cuda.synchronize()
+    n = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        A.group_coefficients(gp, mem, pos, resp_logp, ref, r.R, 0.1, "all_pairs", out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    return {"groups": len(nresp), "responses": int(np.sum(nresp)), "ms": e0.elapsed_time(e1) / n}
 
 
 def main():
@@ -397,8 +440,11 @@ def main():
     log(f"positions {pos_ms * 1e3:.1f} us")
 
     # Packed token log-probs over a Qwen3-sized vocabulary (a next step after attention, reported beside the step).
-    extra["logp"] = logp_rate(A, torch, r, pos_out, ps)
+    extra["logp"], resp_logp = logp_rate(A, torch, r, pos_out, ps)
     log(f"token log-probs: {json.dumps(extra['logp'])}")
+    if (r.R > 0).all():
+        extra["group_coef"] = group_coef_time(A, torch, r, resp_logp)
+        log(f"group coefficients: {json.dumps(extra['group_coef'])}")
 
     peak_meas = measured_mfma_peak(A, torch)
     extra["measured_mfma_peak_tflops"] = peak_meas
@@ -410,6 +456,10 @@ def main():
         extra["copy_GBps"] = gbps
         extra["skip_cost"] = skip_cost(A, torch, max(5, args.steps // 2), 2, gbps)
         log(f"skip cost: {json.dumps(extra['skip_cost'])}")
+
+    if not args.no_baselines:
+        extra["other_workloads"] = config_sweep(A, torch, max(5, args.steps // 2), 2)
+        log(f"other workloads: {json.dumps({k_: round(v_['useful_tflops'], 1) for k_, v_ in extra['other_workloads'].items()})}")
 
     if args.copy_calibration:
         # 2^28 bytes read and 2^28 bytes written per launch, 3 launches.
