@@ -243,10 +243,12 @@ def logp_rate(A, torch, r, pos_out, ps, V=151936):
             "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}, resp
 
 
-def cpu_baseline(w, seconds):
+def cpu_baseline(w, seconds, gpu=None):
     """The fp64 oracle (dense masked attention + naive backward) on a bounded
     sample of the same workload: whole (batch row, kv group) units, in order,
-    until `seconds` of wall time have been spent."""
+    until `seconds` of wall time have been spent.  With `gpu` (the timed
+    run's outputs on the host), its results on the same units are compared
+    with the oracle's, outside the timed region."""
     import torch
     import oracle
     from workloads.generate import descriptor_arrays
@@ -257,15 +259,31 @@ def cpu_baseline(w, seconds):
     pk, br, _ = oracle.token_ids(P, R, ps.B, ps.S)
     G = w.Hq // w.Hkv
     flops, units, t_used = 0.0, [], 0.0
+    err = {"o_max_abs": 0.0, "lse_max_abs": 0.0}
+    sq = {x: [0.0, 0.0] for x in ("o", "dq", "dk", "dv")}  # squared error, squared reference
     for b in range(ps.B):
         mb = oracle.attention_mask(pk, br, row=b)
         n_allowed = int(mb.sum())
+        valid = torch.from_numpy(pk[b] >= 0)
         for g in range(w.Hkv):
             t0 = time.perf_counter()
             rowmask = _RowMask(mb, b)
-            oracle.attn_fwd(w.q, w.k, w.v, rowmask, w.scale, rows=[b], heads=range(g * G, (g + 1) * G))
-            oracle.attn_bwd(w.q, w.k, w.v, w.do, rowmask, w.scale, rows=[b], groups=[g])
+            hs = range(g * G, (g + 1) * G)
+            O, L = oracle.attn_fwd(w.q, w.k, w.v, rowmask, w.scale, rows=[b], heads=hs)
+            dq, dk, dv = oracle.attn_bwd(w.q, w.k, w.v, w.do, rowmask, w.scale, rows=[b], groups=[g])
             t_used += time.perf_counter() - t0
+            if gpu is not None:
+                h0, h1 = g * G, (g + 1) * G
+                pairs = (("o", gpu["o"][b, :, h0:h1], O[b, :, h0:h1]), ("dq", gpu["dq"][b, :, h0:h1], dq[b, :, h0:h1]),
+                         ("dk", gpu["dk"][b, :, g], dk[b, :, g]), ("dv", gpu["dv"][b, :, g], dv[b, :, g]))
+                for name, x, ref in pairs:
+                    x, ref = x[valid].double(), ref[valid]
+                    sq[name][0] += float(((x - ref) ** 2).sum())
+                    sq[name][1] += float((ref ** 2).sum())
+                    if name == "o":
+                        err["o_max_abs"] = max(err["o_max_abs"], float((x - ref).abs().max()))
+                lg, lr = gpu["lse"][b, h0:h1][:, valid].double(), L[b, h0:h1][:, valid]
+                err["lse_max_abs"] = max(err["lse_max_abs"], float((lg - lr).abs().max()))
             flops += 14.0 * w.D * G * n_allowed
             units.append((b, g))
             if t_used >= seconds:
@@ -280,9 +298,13 @@ def cpu_baseline(w, seconds):
                 break
     except OSError:
         pass
-    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(), "kind": "oracle",
-            "sample": f"fp64 oracle fwd+bwd on {len(units)} of {ps.B * w.Hkv} (batch row, kv group) units "
-                      f"({G} q heads each) of the same workload, {t_used:.1f} s wall, useful-FLOP rate; CPU: {cpu}"}
+    out = {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(), "kind": "oracle",
+           "sample": f"fp64 oracle fwd+bwd on {len(units)} of {ps.B * w.Hkv} (batch row, kv group) units "
+                     f"({G} q heads each) of the same workload, {t_used:.1f} s wall, useful-FLOP rate; CPU: {cpu}"}
+    if gpu is not None:
+        err.update({f"{x}_rel_l2": (sq[x][0] / sq[x][1]) ** 0.5 if sq[x][1] > 0 else 0.0 for x in sq})
+        out["parity_on_sample"] = err
+    return out
 
 
 class _RowMask:
@@ -401,7 +423,8 @@ def main():
              "skip_frac_bwd_tiles": totb[2] / max(1, sum(totb)), "tiles_bwd": {"full": totb[0], "partial": totb[1],
              "skip": totb[2], "shape": list(r.btile)},
              "kernels": kern, "frac_of_peak": value / PEAK_BF16_TFLOPS, "allowed_pairs": n_allowed,
-             "useful_flop_per_step": useful, "step_ms_events": per["step_events"]}
+             "useful_flop_per_step": useful, "step_ms_events": per["step_events"],
+             "useful_tflops_map_excluded": useful / ((per["fwd"] + per["bwd_dq"] + per["bwd_dkdv"]) * 1e-3) / 1e12}
 
     if not args.no_baselines:
         rd = Runner(A, torch, ps, q, k, v, do, w.Hq, w.Hkv, w.D, w.scale, dense=True)
@@ -473,8 +496,10 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host ...")
-        cpu = cpu_baseline(w, args.cpu_seconds)
-        log(f"cpu baseline {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+        gpu = {"o": r.o.cpu(), "lse": r.lse.cpu(), "dq": r.dq.cpu(), "dk": r.dk.cpu(), "dv": r.dv.cpu()}
+        cpu = cpu_baseline(w, args.cpu_seconds, gpu)
+        log(f"cpu baseline {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads; parity on that sample: "
+            f"{json.dumps(cpu.get('parity_on_sample'))}")
 
     out = {
         "metric": "useful TFLOP/s packed-attention fwd+bwd (unmasked FLOPs); % bf16 MFMA peak",
