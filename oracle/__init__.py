@@ -22,6 +22,8 @@ method equals ordinary masked softmax attention):
                          per-response sums
   groupdpo               group preference objectives over packs of K
                          responses and their surrogate coefficients
+  rope                   rotary embedding at the packed (branch-aligned)
+                         position ids, and its inverse for gradients
 
 Every function is pinned in tests/ against facts the pages or mathematics
 fix (worked masks, closed-form counts, brute force, finite differences,
@@ -36,3 +38,4 @@ from .attention import (  # noqa: F401
 from .positions import positions  # noqa: F401
 from .logprob import row_logsumexp, token_logp, response_logp  # noqa: F401
 from . import groupdpo  # noqa: F401
+from . import rope  # noqa: F401
