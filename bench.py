@@ -337,6 +337,29 @@ def config_sweep(A, torch, steps, warmup, cfgs=(3, 4, 5)):
     return out
 
 
+def rope_rate(A, torch, r, q, k, base=1e6):
+    """pba_packed_rope on the workload's Q (Hq heads) and K (Hkv heads), out
+    of place: HBM bytes = read + write of each tensor."""
+    yq, yk = torch.empty_like(q), torch.empty_like(k)
+    for _ in range(2):
+        A.packed_rope(r.fmap, q, base, out=yq)
+        A.packed_rope(r.fmap, k, base, out=yk)
+    torch.cuda.synchronize()
+    n = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        A.packed_rope(r.fmap, q, base, out=yq)
+        A.packed_rope(r.fmap, k, base, out=yk)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    nbytes = 2 * (q.numel() + k.numel()) * 2
+    del yq, yk
+    return {"ms_q_and_k": ms, "hbm_bytes": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9,
+            "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
 def group_coef_time(A, torch, r, resp_logp):
     """pba_group_coefficients on the workload's packs (one group per pack,
     response 0 preferred), policy and reference sums from the log-prob run."""
@@ -461,6 +484,10 @@ def main():
     pos_bytes = ps.B * ps.S * (4 + 4 + 16 + 4 + 4 + 1)
     extra["positions"] = {"ms": pos_ms, "GBps": pos_bytes / (pos_ms * 1e-3) / 1e9, "bytes": pos_bytes}
     log(f"positions {pos_ms * 1e3:.1f} us")
+
+    # Rotary embedding at the packed positions (a step before attention, reported beside the step).
+    extra["rope"] = rope_rate(A, torch, r, q, k)
+    log(f"rope: {json.dumps(extra['rope'])}")
 
     # Packed token log-probs over a Qwen3-sized vocabulary (a next step after attention, reported beside the step).
     extra["logp"], resp_logp = logp_rate(A, torch, r, pos_out, ps)

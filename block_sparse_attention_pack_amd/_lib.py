@@ -27,7 +27,7 @@ TILE_SKIP, TILE_PARTIAL, TILE_FULL = 0, 1, 2
 EXPORTED = ("pba_strerror", "pba_fwd_tile", "pba_bwd_tile", "pba_map_bytes", "pba_map_init",
             "pba_pack_block_map", "pba_pack_block_maps", "pba_packed_attn_fwd", "pba_bwd_workspace_bytes", "pba_packed_attn_bwd",
             "pba_packed_attn_bwd_stages", "pba_mfma_probe", "pba_pack_positions",
-            "pba_packed_token_logp", "pba_group_coefficients")
+            "pba_packed_token_logp", "pba_group_coefficients", "pba_packed_rope")
 
 
 class PbaBlockMap(ctypes.Structure):
@@ -80,6 +80,9 @@ _lib.pba_group_coefficients.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_
                                         ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
 _lib.pba_group_coefficients.restype = ctypes.c_int
+_lib.pba_packed_rope.argtypes = [ctypes.POINTER(PbaBlockMap), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                 ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+_lib.pba_packed_rope.restype = ctypes.c_int
 _lib.pba_mfma_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
 _lib.pba_mfma_probe.restype = ctypes.c_int
 BWD_DQ, BWD_DKDV, BWD_ALL = 1, 2, 3
@@ -386,3 +389,18 @@ def group_coefficients(group_ptr, member, positive, pol, ref, resp_len, beta: fl
                                        ptr(nll_w), ptr(loss), status.data_ptr(), _stream(stream)),
            "pba_group_coefficients")
     return coef, nll_w, loss, status
+
+
+def packed_rope(m: BlockMap, x, base: float = 10000.0, inverse: bool = False, out=None, stream=None):
+    """Rotary embedding of x (bf16 [B, S, H, D]) at the map's packed,
+    branch-aligned position ids; inverse=True rotates back (for gradients).
+    out may be x itself (in place)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 [B, S, H, D] tensor")
+    B, S, H, D = x.shape
+    if (B, S) != (m.B, m.S):
+        raise ValueError("x does not match the map's rows")
+    y = torch.empty_like(x) if out is None else out
+    _check(_lib.pba_packed_rope(ctypes.byref(m.struct), x.data_ptr(), y.data_ptr(), H, D, float(base),
+                                int(bool(inverse)), _stream(stream)), "pba_packed_rope")
+    return y

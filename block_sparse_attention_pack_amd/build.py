@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpba.so")
-SOURCES = ["pba_map.hip", "pba_fwd.hip", "pba_bwd.hip", "pba_probe.hip", "pba_logp.hip", "pba_group.hip", "pba_api.cpp"]
+SOURCES = ["pba_map.hip", "pba_fwd.hip", "pba_bwd.hip", "pba_probe.hip", "pba_logp.hip", "pba_group.hip", "pba_rope.hip", "pba_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc")
 FLAGS = [

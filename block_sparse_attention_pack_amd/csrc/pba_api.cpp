@@ -131,7 +131,7 @@ const char* pba_strerror(int code) {
     case PBA_ERR_DEVICE: return "no gfx950 device current, or a HIP launch failed";
     case PBA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
     case PBA_ERR_SCALE: return "softmax scale must be positive and finite";
-    case PBA_ERR_ARG: return "objective unknown, or beta / alpha out of range";
+    case PBA_ERR_ARG: return "objective, beta, alpha or rotary base out of range";
     case PBA_DESC_ROW: return "descriptor: row outside [0, B)";
     case PBA_DESC_NEGATIVE: return "descriptor: negative start, length or response count";
     case PBA_DESC_RESP_RANGE: return "descriptor: response range outside resp_len";
@@ -278,6 +278,28 @@ int pba_packed_token_logp(const pba_block_map* map, const pba_pack* packs, int n
   return pba::launch_token_logp(a, resp_logp ? &r : nullptr, static_cast<hipStream_t>(stream)) == hipSuccess
              ? PBA_OK
              : PBA_ERR_DEVICE;
+}
+
+int pba_packed_rope(const pba_block_map* map, const void* x, void* y, int H, int D, float base, int inverse,
+                    void* stream) {
+  if (!map || !map->status || !map->tok_pack || !map->tok_win || !x || !y) return PBA_ERR_NULL;
+  if (map->B < 1 || map->B > kMaxB || map->S < 1 || map->S > kMaxS || H < 1 || H > kMaxHeads) return PBA_ERR_SHAPE;
+  if (D != 64 && D != 128) return PBA_ERR_HEAD_DIM;
+  if (!(base > 1.f) || !std::isfinite(base)) return PBA_ERR_ARG;
+  if (!aligned16(x) || !aligned16(y)) return PBA_ERR_ALIGN;
+  if (int rc = device_ok()) return rc;
+  pba::RopeArgs a;
+  a.status = map->status;
+  a.tok_pack = map->tok_pack;
+  a.tok_win = map->tok_win;
+  a.x = static_cast<const pba::bf16*>(x);
+  a.y = static_cast<pba::bf16*>(y);
+  a.ntok = (int64_t)map->B * map->S;
+  a.S = map->S;
+  a.H = H;
+  a.log2_base = std::log2(base);
+  a.sign = inverse ? -1.f : 1.f;
+  return pba::launch_rope(a, D, static_cast<hipStream_t>(stream)) == hipSuccess ? PBA_OK : PBA_ERR_DEVICE;
 }
 
 int pba_group_coefficients(const int32_t* group_ptr, int n_groups, const int32_t* member, const uint8_t* positive,

@@ -1,6 +1,6 @@
 // Declarations shared by the kernels of the rows that follow attention
-// (positions, log-prob gathering, group preference coefficients) and the
-// C-ABI layer.
+// (positions, rotary embedding, log-prob gathering, group preference
+// coefficients) and the C-ABI layer.
 #pragma once
 
 #include "pba_internal.h"
@@ -68,5 +68,17 @@ struct GroupArgs {  // group_coef
   int32_t* status;
 };
 hipError_t launch_group_coef(const GroupArgs& a, hipStream_t stream);
+
+struct RopeArgs {  // rope_apply
+  const int32_t* status;
+  const int32_t* tok_pack;
+  const int32_t* tok_win;
+  const bf16* x;
+  bf16* y;
+  int64_t ntok;
+  int S, H;
+  float log2_base, sign;
+};
+hipError_t launch_rope(const RopeArgs& a, int D, hipStream_t stream);
 
 }  // namespace pba

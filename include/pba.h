@@ -23,8 +23,9 @@
  *   pba_packed_attn_fwd  Q, K, V (bf16, grouped heads) -> O (bf16), LSE (fp32)
  *   pba_packed_attn_bwd  dO -> dQ, dK, dV (bf16)
  * and the steps around them in a preference-training step: aligned
- * position ids and log-prob gather rows (pba_pack_positions), packed token
- * log-probs (pba_packed_token_logp) and group preference coefficients
+ * position ids and log-prob gather rows (pba_pack_positions), rotary
+ * embedding at those positions (pba_packed_rope), packed token log-probs
+ * (pba_packed_token_logp) and group preference coefficients
  * (pba_group_coefficients).
  *
  * Conventions shared by every call.
@@ -74,7 +75,7 @@ extern "C" {
 #define PBA_ERR_DEVICE     -8  /* no gfx950 device current, or a HIP launch failed  */
 #define PBA_ERR_ALIGN      -9  /* a tensor pointer is not 16-byte aligned          */
 #define PBA_ERR_SCALE     -10  /* softmax_scale not positive and finite            */
-#define PBA_ERR_ARG       -11  /* objective, beta or alpha out of range            */
+#define PBA_ERR_ARG       -11  /* objective, beta, alpha or rotary base out of range */
 
 /* ---- device status codes (map->status[0]; status[1] = first bad pack) -- */
 #define PBA_DESC_OK          0
@@ -232,6 +233,27 @@ PBA_API int pba_packed_token_logp(const pba_block_map* map, const pba_pack* pack
                                   const int32_t* resp_len, int n_resp_total, const int32_t* src_row,
                                   const uint8_t* loss_mask, const void* logits, int V, const int32_t* tokens,
                                   float* tok_logp, float* resp_logp, void* stream);
+
+/* Rotary embedding at the packed, branch-aligned position ids ("DPO
+ * Preference Packing: Dense Masks and Sparse Execution", section "Layout
+ * requirements": every response keeps the positions of its own
+ * [prompt | response] sequence; the ids are those pba_pack_positions writes,
+ * pad tokens 0).  For every token t and head h of x (bf16 [B, S, H, D],
+ * device, 16-byte aligned; y the same shape, may be x itself):
+ *   y[t,h,i]       = x[t,h,i] cos(a) - x[t,h,i+D/2] sin(a)
+ *   y[t,h,i+D/2]   = x[t,h,i] sin(a) + x[t,h,i+D/2] cos(a),   i < D/2,
+ *   a = pos(t) * base^(-2i/D), negated when inverse != 0
+ * (rotate-half pairing; the inverse is the transpose rotation, which maps
+ * gradients with respect to the rotated tensor to gradients with respect to
+ * x).  Angles and products in fp32, output rounded to bf16.  Map from
+ * pba_pack_block_map(s) for (B, S) (any tile shape); nothing is written when
+ * its status is not OK.  Apply it to Q (H = Hq) and K (H = Hkv) before the
+ * forward, and with inverse = 1 to dQ and dK after the backward.  Returns
+ * PBA_OK, PBA_ERR_NULL, PBA_ERR_SHAPE, PBA_ERR_HEAD_DIM (D not 64 or 128),
+ * PBA_ERR_ARG (base not above 1 and finite), PBA_ERR_ALIGN or
+ * PBA_ERR_DEVICE. */
+PBA_API int pba_packed_rope(const pba_block_map* map, const void* x, void* y, int H, int D, float base, int inverse,
+                            void* stream);
 
 /* Group preference objectives and their surrogate coefficients ("GroupDPO"
  * page, section "core formulas").  A batch holds n_groups groups in CSR

@@ -130,3 +130,18 @@ def test_group_coefficients_argument_errors():
     assert call(alpha=-1.0) == -11
     assert call(alpha=float("nan")) == -11
     assert "group" in P.api.strerror(15) and "objective" in P.api.strerror(-11)
+
+
+def test_rope_argument_errors():
+    import block_sparse_attention_pack_amd as P
+    A = P.api
+    lib = A._lib
+    m = A.PbaBlockMap()
+    assert lib.pba_map_init(ctypes.byref(m), 256, 1 << 20, 2, 100, 64, 64) == 0
+    assert lib.pba_packed_rope(None, 16, 16, 2, 64, 1e4, 0, None) == -1
+    assert lib.pba_packed_rope(ctypes.byref(m), None, 16, 2, 64, 1e4, 0, None) == -1
+    assert lib.pba_packed_rope(ctypes.byref(m), 16, 16, 0, 64, 1e4, 0, None) == -2
+    assert lib.pba_packed_rope(ctypes.byref(m), 16, 16, 2, 96, 1e4, 0, None) == -4
+    assert lib.pba_packed_rope(ctypes.byref(m), 16, 16, 2, 64, 1.0, 0, None) == -11
+    assert lib.pba_packed_rope(ctypes.byref(m), 16, 16, 2, 64, float("inf"), 0, None) == -11
+    assert lib.pba_packed_rope(ctypes.byref(m), 24, 16, 2, 64, 1e4, 0, None) == -9

@@ -1,0 +1,127 @@
+"""GPU rotary embedding at packed positions vs the oracle (fp64).
+
+Tolerance, per element: the output is rounded to bf16 (half an ulp,
+2^-9 relative) and the angle pos * base^(-2i/D) is formed in fp32 (relative
+error about 2^-22, i.e. at most 2.5e-3 rad for positions below 10^4), so
+|y - y_ref| <= 2^-8 |y_ref| + 3e-3 (|x_i| + |x_{i+D/2}|)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import rope as R
+from gpu_path import api, build_map, say
+from workloads.generate import descriptor_arrays, make_packset, random_packset
+
+pytestmark = pytest.mark.gpu
+
+
+def _bound_ok(x, y, yref):
+    D = x.shape[-1]
+    xs = x.abs()
+    pair = torch.cat([xs[..., : D // 2] + xs[..., D // 2:]] * 2, dim=-1)
+    return bool(((y - yref).abs() <= 2.0 ** -8 * yref.abs() + 3e-3 * pair).all())
+
+
+def _run(ps, H, D, base, seed, inverse=False, in_place=False):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((ps.B, ps.S, H, D), generator=g).to(torch.bfloat16)
+    m = build_map(ps, 64, 64)
+    A = api()
+    xd = x.cuda()
+    y = A.packed_rope(m, xd, base, inverse, out=xd if in_place else None)
+    torch.cuda.synchronize()
+    P, Rl = descriptor_arrays(ps)
+    pos, _, _, _ = oracle.positions(P, Rl, ps.B, ps.S)
+    yref = R.packed_rope(x.double(), pos, base, inverse)
+    return x.double(), y.cpu().double(), yref
+
+
+@pytest.mark.parametrize("cfg,H,D", [(1, 2, 64), (2, 32, 128), (2, 8, 128), (5, 8, 128)])
+def test_workloads(cfg, H, D):
+    ps = make_packset(cfg)
+    say("rope", cfg, H, D, ps.B, ps.S)
+    x, y, yref = _run(ps, H, D, 1e6, cfg)
+    assert _bound_ok(x, y, yref)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_ragged_inverse_and_in_place(seed):
+    rng = np.random.default_rng(900 + seed)
+    ps = random_packset(rng, B=int(rng.integers(1, 4)), S=int(rng.integers(1, 500)), max_packs_per_row=4,
+                        max_resp=4, max_len=int(rng.integers(2, 150)))
+    D = (64, 128)[seed % 2]
+    H = int(rng.integers(1, 7))
+    say("rope random", seed, ps.B, ps.S, H, D)
+    x, y, yref = _run(ps, H, D, 10000.0, seed, inverse=bool(seed & 1), in_place=seed >= 2)
+    assert _bound_ok(x, y, yref)
+
+
+def test_pad_is_identity_and_round_trip():
+    ps = make_packset(2)
+    A = api()
+    m = build_map(ps, 64, 64)
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn((ps.B, ps.S, 8, 128), generator=g).to(torch.bfloat16).cuda()
+    y = A.packed_rope(m, x, 1e6)
+    z = A.packed_rope(m, y, 1e6, inverse=True)
+    torch.cuda.synchronize()
+    P, Rl = descriptor_arrays(ps)
+    pk = oracle.token_ids(P, Rl, ps.B, ps.S)[0]
+    pad = torch.from_numpy(pk < 0)
+    assert torch.equal(y.cpu()[pad], x.cpu()[pad])
+    # forward then inverse: back to x up to two bf16 roundings
+    err = (z.float() - x.float()).abs()
+    assert bool((err <= 2.0 ** -7 * x.float().abs() + 2e-2).all())
+
+
+def test_invalid_map_writes_nothing():
+    A = api()
+    ps = make_packset(1)
+    P, Rl = descriptor_arrays(ps)
+    P = P.copy()
+    P[0, 0] = 5  # row outside [0, B)
+    pd, rd = A.descriptors_to_device(P, Rl)
+    m = A.pack_block_map(pd, rd, ps.B, ps.S, 64, 64)
+    x = torch.ones((ps.B, ps.S, 2, 64), dtype=torch.bfloat16, device="cuda")
+    y = torch.full_like(x, 7.0)
+    A.packed_rope(m, x, 1e4, out=y)
+    torch.cuda.synchronize()
+    assert (y == 7.0).all()
+
+
+def test_packed_rope_attention_equals_pairwise():
+    """Content vectors -> pba_packed_rope -> packed forward equals, on every
+    response row, causal attention over that response's own [prompt |
+    response] sequence rotated at positions 0..n-1 (the oracle), for the
+    Qwen3-8B-shaped packs at reduced width (the property aligned positions
+    exist for: "DPO Preference Packing", section "Layout requirements")."""
+    from workloads.generate import make_workload
+    A = api()
+    w = make_workload(2, 0)
+    ps = w.packset
+    H, D = 4, 128
+    g = torch.Generator().manual_seed(11)
+    xq, xk, xv = (torch.randn((ps.B, ps.S, H, D), generator=g) for _ in range(3))
+    xq, xk, xv = (t.to(torch.bfloat16) for t in (xq, xk, xv))
+    fm = build_map(ps, *A.fwd_tile(H, H, D))
+    q = A.packed_rope(fm, xq.cuda(), 1e6)
+    k = A.packed_rope(fm, xk.cuda(), 1e6)
+    o, lse = A.packed_attn_fwd(fm, q, k, xv.cuda().contiguous(), 1.0 / 128 ** 0.5)
+    torch.cuda.synchronize()
+    o = o.cpu().double()
+    say("rope + attention vs pairwise", ps.B, ps.S)
+    for pk in ps.packs:
+        prompt = list(range(pk.start, pk.start + pk.prompt_len))
+        at = pk.start + pk.prompt_len
+        for r in pk.resp_lens:
+            rows = prompt + list(range(at, at + r))
+            at += r
+            n = len(rows)
+            qq = R.rope(xq[pk.row, rows].double(), list(range(n)), 1e6)[None]
+            kk = R.rope(xk[pk.row, rows].double(), list(range(n)), 1e6)[None]
+            vv = xv[pk.row, rows].double()[None]
+            O, _ = oracle.attn_fwd(qq, kk, vv, np.tril(np.ones((1, n, n), dtype=bool)), 1.0 / 128 ** 0.5)
+            got = o[pk.row, rows[len(prompt):]]
+            ref = O[0, len(prompt):]
+            assert float((got - ref).abs().max()) <= 2e-2, float((got - ref).abs().max())
