@@ -27,7 +27,7 @@ TILE_SKIP, TILE_PARTIAL, TILE_FULL = 0, 1, 2
 EXPORTED = ("pba_strerror", "pba_fwd_tile", "pba_bwd_tile", "pba_map_bytes", "pba_map_init",
             "pba_pack_block_map", "pba_pack_block_maps", "pba_packed_attn_fwd", "pba_bwd_workspace_bytes", "pba_packed_attn_bwd",
             "pba_packed_attn_bwd_stages", "pba_mfma_probe", "pba_pack_positions",
-            "pba_packed_token_logp", "pba_group_coefficients", "pba_packed_rope")
+            "pba_packed_token_logp", "pba_group_coefficients", "pba_packed_rope", "pba_packed_attn_bwd_rope")
 
 
 class PbaBlockMap(ctypes.Structure):
@@ -83,6 +83,9 @@ _lib.pba_group_coefficients.restype = ctypes.c_int
 _lib.pba_packed_rope.argtypes = [ctypes.POINTER(PbaBlockMap), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                  ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
 _lib.pba_packed_rope.restype = ctypes.c_int
+_lib.pba_packed_attn_bwd_rope.argtypes = list(_lib.pba_packed_attn_bwd.argtypes[:-2]) + [ctypes.c_float, ctypes.c_float,
+                                                                                        ctypes.c_void_p]
+_lib.pba_packed_attn_bwd_rope.restype = ctypes.c_int
 _lib.pba_mfma_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
 _lib.pba_mfma_probe.restype = ctypes.c_int
 BWD_DQ, BWD_DKDV, BWD_ALL = 1, 2, 3
@@ -286,6 +289,36 @@ def packed_attn_bwd(qmap: BlockMap, kmap: BlockMap, q, k, v, o, lse, dout, softm
                                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), base + off,
                                            workspace.numel() - off, B, S, Hq, Hkv, D, scale, _stream(stream)),
            "pba_packed_attn_bwd_stages")
+    return dq, dk, dv
+
+
+def packed_attn_bwd_rope(qmap: BlockMap, kmap: BlockMap, q_rot, k_rot, v, o, lse, dout, rope_base: float,
+                         softmax_scale: Optional[float] = None,
+                         out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None):
+    """dQ, dK (with respect to the unrotated Q and K) and dV for inputs
+    rotated by packed_rope(..., rope_base): the inverse rotation of the
+    gradients runs inside the backward kernels."""
+    for n, x in (("q_rot", q_rot), ("k_rot", k_rot), ("v", v), ("o", o), ("dout", dout)):
+        _bf16(x, n)
+    B, S, Hq, D = q_rot.shape
+    Hkv = k_rot.shape[2]
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q_rot), torch.empty_like(k_rot), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+    need = workspace_bytes(B, S, Hq, D)
+    if workspace is None:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=q_rot.device)
+    base = workspace.data_ptr()
+    off = (-base) % 256
+    _check(_lib.pba_packed_attn_bwd_rope(ctypes.byref(qmap.struct), ctypes.byref(kmap.struct), q_rot.data_ptr(),
+                                         k_rot.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), base + off,
+                                         workspace.numel() - off, B, S, Hq, Hkv, D, scale, float(rope_base),
+                                         _stream(stream)),
+           "pba_packed_attn_bwd_rope")
     return dq, dk, dv
 
 

@@ -370,10 +370,13 @@ size_t pba_bwd_workspace_bytes(int B, int S, int Hq, int D) {
   return 2 * align_up((size_t)B * Hq * S * 4);
 }
 
-int pba_packed_attn_bwd_stages(int stages, const pba_block_map* qmap, const pba_block_map* kmap, const void* q,
-                               const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int S,
-                               int Hq, int Hkv, int D, float softmax_scale, void* stream) {
+}  // extern "C"
+
+namespace {
+int bwd_impl(int stages, const pba_block_map* qmap, const pba_block_map* kmap, const void* q, const void* k,
+             const void* v, const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes, int B, int S, int Hq, int Hkv, int D, float softmax_scale,
+             float rope_base, void* stream) {
   if (stages < 1 || stages > PBA_BWD_ALL) return PBA_ERR_SHAPE;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return PBA_ERR_NULL;
   if (int rc = check_heads(B, S, Hq, Hkv, D)) return rc;
@@ -412,8 +415,29 @@ int pba_packed_attn_bwd_stages(int stages, const pba_block_map* qmap, const pba_
   a.G = Hq / Hkv;
   a.scale = softmax_scale;
   a.scale_log2 = softmax_scale * pba::kLog2eHost;
+  a.rope_log2_base = rope_base > 0.f ? std::log2(rope_base) : 0.f;
   hipError_t e = pba::launch_bwd(a, D, stages, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PBA_OK : PBA_ERR_DEVICE;
+}
+}  // namespace
+
+extern "C" {
+
+int pba_packed_attn_bwd_stages(int stages, const pba_block_map* qmap, const pba_block_map* kmap, const void* q,
+                               const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int S,
+                               int Hq, int Hkv, int D, float softmax_scale, void* stream) {
+  return bwd_impl(stages, qmap, kmap, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, S, Hq, Hkv, D,
+                  softmax_scale, 0.f, stream);
+}
+
+int pba_packed_attn_bwd_rope(const pba_block_map* qmap, const pba_block_map* kmap, const void* q_rot,
+                             const void* k_rot, const void* v, const void* o, const float* lse, const void* dout,
+                             void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int S,
+                             int Hq, int Hkv, int D, float softmax_scale, float rope_base, void* stream) {
+  if (!(rope_base > 1.f) || !std::isfinite(rope_base)) return PBA_ERR_ARG;
+  return bwd_impl(PBA_BWD_ALL, qmap, kmap, q_rot, k_rot, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B,
+                  S, Hq, Hkv, D, softmax_scale, rope_base, stream);
 }
 
 int pba_packed_attn_bwd(const pba_block_map* qmap, const pba_block_map* kmap, const void* q, const void* k,

@@ -250,6 +250,9 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
     a.delta[((int64_t)b * Hq + h) * S + qi] = delta;
     a.lse2[((int64_t)b * Hq + h) * S + qi] = l2;
   }
+  // With rotary inputs, dQ is rotated back to the unrotated Q's frame at
+  // the query's packed position (its row is 0 where the query is pad).
+  if (a.rope_log2_base != 0.f) rope_rotate_t<C::NE>(dq, (wphi - wplo) + (qi - wlo), hi, a.rope_log2_base, -1.f);
   // dQ (bf16, times the softmax scale) through LDS, free after the last
   // barrier, so that its rows leave as whole contiguous segments.
   {
@@ -368,7 +371,7 @@ __device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D
 // 32e + 8*(r/4) + 4*hi + r%4), from which the workgroup stores whole rows.
 template <int D, int LSTR>
 __device__ __forceinline__ void pair_sum_lds(const f32x16 (&acc)[D / 32], float* slot, int qh, char* rows, int krow,
-                                             int hi, float scale) {
+                                             int hi, float scale, bool rope, int pos, float log2_base) {
   constexpr int NE = D / 32;
   if (qh == 1) {
 #pragma unroll
@@ -380,15 +383,26 @@ __device__ __forceinline__ void pair_sum_lds(const f32x16 (&acc)[D / 32], float*
   }
   __syncthreads();
   if (qh == 0) {
-    char* row = rows + krow * LSTR + 8 * hi;
+    f32x16 sum[NE];
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const f32x4 o = *(const f32x4*)(slot + 16 * e + 4 * rg);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sum[e][4 * rg + t] = acc[e][4 * rg + t] + o[t];
+      }
+    }
+    // With rotary inputs, dK is rotated back at the key's packed position.
+    if (rope) rope_rotate_t<NE>(sum, pos, hi, log2_base, -1.f);
+    char* row = rows + krow * LSTR + 8 * hi;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
         bf16x4 v;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) v[t] = (bf16)((acc[e][4 * rg + t] + o[t]) * scale);
+        for (int t = 0; t < 4; ++t) v[t] = (bf16)(sum[e][4 * rg + t] * scale);
         *(bf16x4*)(row + 2 * (32 * e + 8 * rg)) = v;
       }
     }
@@ -427,7 +441,8 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   const int g = blockIdx.x % Hkv;
   const int b = item / mp.nkt, kt = item % mp.nkt;
   const int kj = kt * 128 + 32 * kb + l32;  // this lane's key
-  const int qend = kj < S ? reinterpret_cast<const int4*>(mp.tok_win)[(int64_t)b * S + kj].w : kj;
+  const int4 kwin = reinterpret_cast<const int4*>(mp.tok_win)[(int64_t)b * S + min(kj, S - 1)];
+  const int qend = kj < S ? kwin.w : kj;
 
   const int64_t lrow = (int64_t)b * mp.nkt + kt;
   const cint_ptr cnt = cptr(mp.k2q_cnt) + lrow * 2;
@@ -502,8 +517,10 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   // areas, free after the loop, and leave as whole rows.
   using Blk = RowBlock<128, D * 2>;
   static_assert(128 * Blk::LSTR <= 128 * C::STR * 2, "a dK / dV block fits the K / V area");
-  pair_sum_lds<D, Blk::LSTR>(dkt, slot, qh, (char*)sK, 32 * kb + l32, hi, a.scale);
-  pair_sum_lds<D, Blk::LSTR>(dvt, slot, qh, (char*)sV, 32 * kb + l32, hi, 1.f);
+  const int kpos = (kwin.z - kwin.y) + (kj - kwin.x);  // the key's packed position (rows past S are not stored)
+  pair_sum_lds<D, Blk::LSTR>(dkt, slot, qh, (char*)sK, 32 * kb + l32, hi, a.scale, a.rope_log2_base != 0.f, kpos,
+                             a.rope_log2_base);
+  pair_sum_lds<D, Blk::LSTR>(dvt, slot, qh, (char*)sV, 32 * kb + l32, hi, 1.f, false, 0, 0.f);
   const int krows = min(128, S - kt * 128);
   const int64_t out = ((int64_t)b * S + kt * 128) * kvstride + (int64_t)g * D;
   Blk::template store<512>(a.dk + out, (const char*)sK, krows, kvstride * 2, tid);

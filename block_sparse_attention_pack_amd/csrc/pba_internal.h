@@ -63,6 +63,10 @@ struct BwdArgs {
   float* lse2;   // [B, Hq, S] fp32 LSE * log2(e) (0 for rows that see nothing)
   int B, S, Hq, Hkv, G;
   float scale, scale_log2;
+  // log2 of the rotary base when dQ and dK are rotated back to the
+  // unrotated Q and K (the inputs were rotated at the packed positions);
+  // 0 = no rotation.
+  float rope_log2_base;
 };
 
 constexpr float kLog2eHost = 1.4426950408889634f;

@@ -70,6 +70,31 @@ __host__ __device__ __forceinline__ KeyMask key_mask(int lim, int lo, int pc, in
   const unsigned long long m = key_run_bits(lo, end) | key_run_bits(-pc, pend);
   return {(unsigned)m, (unsigned)(m >> 32)};
 }
+// Rotary embedding of an MFMA accumulator block in the transposed layout
+// (lane: one token; register r of block e: head dim 32*e + 8*(r/4) + 4*hi +
+// r%4), rotate-half pairing: dim d < D/2 pairs with d + D/2, i.e. block e
+// with block e + NE/2 in the same lane and register.  The angle is
+// sign * pos * base^(-2d/D), reduced to revolutions in fp32 before the
+// hardware sine and cosine (which take revolutions).
+template <int NE>
+__device__ __forceinline__ void rope_rotate_t(f32x16 (&acc)[NE], int pos, int hi, float log2_base, float sign) {
+  constexpr int D = 32 * NE;
+  const float p = sign * (float)pos * 0.15915494309189535f;  // pos / (2 pi)
+#pragma unroll
+  for (int e = 0; e < NE / 2; ++e) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int d = 32 * e + 8 * (r >> 2) + 4 * hi + (r & 3);
+      float rev = p * exp2f(-(float)(2 * d) / (float)D * log2_base);
+      rev -= floorf(rev);
+      const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+      const float u = acc[e][r], v = acc[e + NE / 2][r];
+      acc[e][r] = u * cs - v * sn;
+      acc[e + NE / 2][r] = u * sn + v * cs;
+    }
+  }
+}
+
 // All ones if bit `bit` (a constant after unrolling) of w is set, else 0
 // (one bit-field extract).
 __device__ __forceinline__ int mask_bit(unsigned w, int bit) { return __builtin_amdgcn_sbfe((int)w, bit, 1); }

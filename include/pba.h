@@ -347,6 +347,20 @@ PBA_API int pba_packed_attn_bwd_stages(int stages, const pba_block_map* qmap, co
                                        size_t workspace_bytes, int B, int S, int Hq, int Hkv, int D,
                                        float softmax_scale, void* stream);
 
+/* Backward for rotary inputs, with the rotation of the gradients fused in.
+ * q_rot, k_rot are Q and K rotated by pba_packed_rope at the packed
+ * positions (with this base); o and lse come from pba_packed_attn_fwd on
+ * them.  Writes dV and the gradients with respect to the UNROTATED Q and K
+ * (dQ, dK rotated back at each token's packed position inside the kernels'
+ * epilogues, in fp32 before the bf16 rounding), so no inverse rotation pass
+ * is needed.  Everything else as pba_packed_attn_bwd; rope_base must be
+ * above 1 and finite (PBA_ERR_ARG). */
+PBA_API int pba_packed_attn_bwd_rope(const pba_block_map* qmap, const pba_block_map* kmap, const void* q_rot,
+                                     const void* k_rot, const void* v, const void* o, const float* lse,
+                                     const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                                     size_t workspace_bytes, int B, int S, int Hq, int Hkv, int D,
+                                     float softmax_scale, float rope_base, void* stream);
+
 /* Measurement helper, not an operation of the method: enqueues n_blocks
  * workgroups of 256 threads that each run `iters` iterations of 16 bf16
  * MFMAs (v_mfma_f32_32x32x16_bf16, 32768 FLOP each) per wave, i.e.

@@ -125,3 +125,73 @@ def test_packed_rope_attention_equals_pairwise():
             got = o[pk.row, rows[len(prompt):]]
             ref = O[0, len(prompt):]
             assert float((got - ref).abs().max()) <= 2e-2, float((got - ref).abs().max())
+
+
+def _rope_case(w, base):
+    """GPU: rotate Q, K at the packed positions, forward, fused-rotation
+    backward.  Oracle inputs: the same bf16 Q, K, V, dO."""
+    A = api()
+    ps = w.packset
+    q, k, v, do = (x.cuda().contiguous() for x in (w.q, w.k, w.v, w.do))
+    fm = build_map(ps, *A.fwd_tile(w.Hq, w.Hkv, w.D))
+    bm = build_map(ps, *A.bwd_tile(w.Hq, w.Hkv, w.D))
+    qr, kr = A.packed_rope(fm, q, base), A.packed_rope(fm, k, base)
+    o, lse = A.packed_attn_fwd(fm, qr, kr, v, w.scale)
+    dq, dk, dv = A.packed_attn_bwd_rope(fm, bm, qr, kr, v, o, lse, do, base, w.scale)
+    # the same through the unfused path: plain backward, then inverse rotation passes
+    dq_r, dk_r, dv_u = A.packed_attn_bwd(fm, bm, qr, kr, v, o, lse, do, w.scale)
+    dq_u, dk_u = A.packed_rope(fm, dq_r, base, inverse=True), A.packed_rope(fm, dk_r, base, inverse=True)
+    torch.cuda.synchronize()
+    P, Rl = descriptor_arrays(ps)
+    pos = oracle.positions(P, Rl, ps.B, ps.S)[0]
+    return {"o": o.cpu(), "dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu(), "dq_u": dq_u.cpu(), "dk_u": dk_u.cpu(),
+            "dv_u": dv_u.cpu(), "pos": pos, "P": P, "R": Rl}
+
+
+def _rel(x, ref):
+    x, ref = x.double(), ref.double()
+    return float((x - ref).norm() / ref.norm())
+
+
+def test_fused_rope_backward_tiny_vs_oracle():
+    from workloads.generate import make_workload
+    w = make_workload(1, 0, unscaled=True)
+    base = 1e4
+    got = _rope_case(w, base)
+    ps = w.packset
+    pk, br, _ = oracle.token_ids(got["P"], got["R"], ps.B, ps.S)
+    mask = oracle.attention_mask(pk, br)
+    qr, kr = R.packed_rope(w.q, got["pos"], base), R.packed_rope(w.k, got["pos"], base)
+    O, _ = oracle.attn_fwd(qr, kr, w.v, mask, w.scale)
+    dqr, dkr, dv = oracle.attn_bwd(qr, kr, w.v, w.do, mask, w.scale)
+    dq, dk = R.packed_rope(dqr, got["pos"], base, inverse=True), R.packed_rope(dkr, got["pos"], base, inverse=True)
+    say("fused rope bwd tiny", _rel(got["dq"], dq), _rel(got["dk"], dk), _rel(got["dv"], dv))
+    assert _rel(got["o"], O) <= 1e-2
+    for name, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert _rel(got[name], ref) <= 1e-2, name
+        assert _rel(got[name + "_u"], ref) <= 1e-2, name + " unfused"
+
+
+def test_fused_rope_backward_qwen3_packs_sampled():
+    from workloads.generate import make_workload
+    w = make_workload(2, 0, unscaled=True)
+    base = 1e6
+    got = _rope_case(w, base)
+    ps = w.packset
+    pk, br, _ = oracle.token_ids(got["P"], got["R"], ps.B, ps.S)
+    rng = np.random.default_rng(5)
+    b, g = int(rng.integers(0, ps.B)), int(rng.integers(0, w.Hkv))
+    valid = np.nonzero(pk[b] >= 0)[0]
+    qrows = np.sort(rng.choice(valid, size=64, replace=False))
+    krows = np.sort(rng.choice(valid, size=64, replace=False))
+    mb = oracle.attention_mask(pk, br, row=b)
+    qr, kr = R.packed_rope(w.q, got["pos"], base), R.packed_rope(w.k, got["pos"], base)
+    dqs, dks, dvs = oracle.attn_bwd_sampled(qr, kr, w.v, w.do, mb, b, g, qrows, krows, w.scale)
+    G = w.Hq // w.Hkv
+    pos_b = got["pos"][b]
+    dq_ref = R.rope(dqs.permute(1, 0, 2), pos_b[qrows], base, inverse=True).permute(1, 0, 2)  # [G, n, D]
+    dk_ref = R.rope(dks[:, None], pos_b[krows], base, inverse=True)[:, 0]
+    dq = torch.stack([got["dq"][b, qrows, h] for h in range(g * G, (g + 1) * G)])
+    e = (_rel(dq, dq_ref), _rel(got["dk"][b, krows, g], dk_ref), _rel(got["dv"][b, krows, g], dvs))
+    say("fused rope bwd qwen3 packs sampled", b, g, e)
+    assert max(e) <= 1e-2, e
