@@ -360,6 +360,47 @@ def rope_rate(A, torch, r, q, k, base=1e6):
             "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
+def rope_step_cost(A, torch, r, q, k, v, do, scale, base=1e6, n=10):
+    """The attention step with rotary inputs two ways: unfused (rotation
+    passes on Q and K, plain forward and backward, inverse passes on dQ and
+    dK) and fused (K pass, forward rotating Q in registers and writing the
+    rotated Q, backward rotating dQ and dK back in its epilogues)."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    qr, kr = torch.empty_like(q), torch.empty_like(k)
+    o, lse = torch.empty_like(q), torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32,
+                                               device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def unfused():
+        A.packed_rope(r.fmap, q, base, out=qr)
+        A.packed_rope(r.fmap, k, base, out=kr)
+        A.packed_attn_fwd(r.fmap, qr, kr, v, scale, out=(o, lse))
+        A.packed_attn_bwd(r.fmap, r.bmap, qr, kr, v, o, lse, do, scale, out=(dq, dk, dv), workspace=r.ws)
+        A.packed_rope(r.fmap, dq, base, inverse=True, out=dq)
+        A.packed_rope(r.fmap, dk, base, inverse=True, out=dk)
+
+    def fused():
+        A.packed_rope(r.fmap, k, base, out=kr)
+        A.packed_attn_fwd_rope(r.fmap, q, kr, v, base, scale, out=(o, lse), q_rot_out=qr)
+        A.packed_attn_bwd_rope(r.fmap, r.bmap, qr, kr, v, o, lse, do, base, scale, out=(dq, dk, dv), workspace=r.ws)
+
+    out = {}
+    for name, fn in (("unfused_ms", unfused), ("fused_ms", fused)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) / n
+    out["base"] = base
+    del qr, kr, o, lse, dq, dk, dv
+    return out
+
+
 def group_coef_time(A, torch, r, resp_logp):
     """pba_group_coefficients on the workload's packs (one group per pack,
     response 0 preferred), policy and reference sums from the log-prob run."""
@@ -487,6 +528,7 @@ def main():
 
     # Rotary embedding at the packed positions (a step before attention, reported beside the step).
     extra["rope"] = rope_rate(A, torch, r, q, k)
+    extra["rope"]["attention_step"] = rope_step_cost(A, torch, r, q, k, v, do, w.scale)
     log(f"rope: {json.dumps(extra['rope'])}")
 
     # Packed token log-probs over a Qwen3-sized vocabulary (a next step after attention, reported beside the step).

@@ -27,7 +27,8 @@ TILE_SKIP, TILE_PARTIAL, TILE_FULL = 0, 1, 2
 EXPORTED = ("pba_strerror", "pba_fwd_tile", "pba_bwd_tile", "pba_map_bytes", "pba_map_init",
             "pba_pack_block_map", "pba_pack_block_maps", "pba_packed_attn_fwd", "pba_bwd_workspace_bytes", "pba_packed_attn_bwd",
             "pba_packed_attn_bwd_stages", "pba_mfma_probe", "pba_pack_positions",
-            "pba_packed_token_logp", "pba_group_coefficients", "pba_packed_rope", "pba_packed_attn_bwd_rope")
+            "pba_packed_token_logp", "pba_group_coefficients", "pba_packed_rope", "pba_packed_attn_bwd_rope",
+            "pba_packed_attn_fwd_rope")
 
 
 class PbaBlockMap(ctypes.Structure):
@@ -86,6 +87,9 @@ _lib.pba_packed_rope.restype = ctypes.c_int
 _lib.pba_packed_attn_bwd_rope.argtypes = list(_lib.pba_packed_attn_bwd.argtypes[:-2]) + [ctypes.c_float, ctypes.c_float,
                                                                                         ctypes.c_void_p]
 _lib.pba_packed_attn_bwd_rope.restype = ctypes.c_int
+_lib.pba_packed_attn_fwd_rope.argtypes = [ctypes.POINTER(PbaBlockMap)] + [ctypes.c_void_p] * 6 + [ctypes.c_int] * 5 + \
+    [ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
+_lib.pba_packed_attn_fwd_rope.restype = ctypes.c_int
 _lib.pba_mfma_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
 _lib.pba_mfma_probe.restype = ctypes.c_int
 BWD_DQ, BWD_DKDV, BWD_ALL = 1, 2, 3
@@ -290,6 +294,35 @@ def packed_attn_bwd(qmap: BlockMap, kmap: BlockMap, q, k, v, o, lse, dout, softm
                                            workspace.numel() - off, B, S, Hq, Hkv, D, scale, _stream(stream)),
            "pba_packed_attn_bwd_stages")
     return dq, dk, dv
+
+
+def packed_attn_fwd_rope(m: BlockMap, q, k_rot, v, rope_base: float, softmax_scale: Optional[float] = None,
+                         out=None, q_rot_out=True, stream=None):
+    """(o, lse, q_rot): forward for rotary inputs with Q's rotation fused in
+    (q unrotated, k_rot from packed_rope).  q_rot_out: True to allocate the
+    rotated Q the kernel writes for the backward, a tensor to write it
+    there, or None/False not to write it."""
+    for n, x in (("q", q), ("k_rot", k_rot), ("v", v)):
+        _bf16(x, n)
+    B, S, Hq, D = q.shape
+    Hkv = k_rot.shape[2]
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    if q_rot_out is True:
+        q_rot = torch.empty_like(q)
+    elif q_rot_out is None or q_rot_out is False:
+        q_rot = None
+    else:
+        q_rot = q_rot_out
+    _check(_lib.pba_packed_attn_fwd_rope(ctypes.byref(m.struct), q.data_ptr(), k_rot.data_ptr(), v.data_ptr(),
+                                         o.data_ptr(), lse.data_ptr(), None if q_rot is None else q_rot.data_ptr(),
+                                         B, S, Hq, Hkv, D, scale, float(rope_base), _stream(stream)),
+           "pba_packed_attn_fwd_rope")
+    return o, lse, q_rot
 
 
 def packed_attn_bwd_rope(qmap: BlockMap, kmap: BlockMap, q_rot, k_rot, v, o, lse, dout, rope_base: float,

@@ -337,13 +337,17 @@ int pba_pack_block_map(const pba_pack* packs, int n_packs, const int32_t* resp_l
   return pba_pack_block_maps(packs, n_packs, resp_len, n_resp_total, map, 1, stream);
 }
 
-int pba_packed_attn_fwd(const pba_block_map* map, const void* q, const void* k, const void* v, void* o, float* lse,
-                        int B, int S, int Hq, int Hkv, int D, float softmax_scale, void* stream) {
+}  // extern "C"
+
+namespace {
+int fwd_impl(const pba_block_map* map, const void* q, const void* k, const void* v, void* o, float* lse, void* q_rot,
+             int B, int S, int Hq, int Hkv, int D, float softmax_scale, float rope_base, void* stream) {
   if (!q || !k || !v || !o || !lse) return PBA_ERR_NULL;
   if (int rc = check_heads(B, S, Hq, Hkv, D)) return rc;
   if (int rc = check_scale(softmax_scale)) return rc;
   if (int rc = check_row_bytes(S, Hq, D)) return rc;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return PBA_ERR_ALIGN;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (q_rot && !aligned16(q_rot)))
+    return PBA_ERR_ALIGN;
   int bm, bn;
   pba_fwd_tile(Hq, Hkv, D, &bm, &bn);
   if (int rc = check_map(map, B, S, bm, bn)) return rc;
@@ -361,8 +365,25 @@ int pba_packed_attn_fwd(const pba_block_map* map, const void* q, const void* k, 
   a.G = Hq / Hkv;
   a.wg_heads = pba::fwd_wg_heads(a.G);
   a.scale_log2 = softmax_scale * pba::kLog2eHost;
+  a.rope_log2_base = rope_base > 0.f ? std::log2(rope_base) : 0.f;
+  a.q_rot = static_cast<pba::bf16*>(q_rot);
   hipError_t e = pba::launch_fwd(a, D, B, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PBA_OK : PBA_ERR_DEVICE;
+}
+}  // namespace
+
+extern "C" {
+
+int pba_packed_attn_fwd(const pba_block_map* map, const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int S, int Hq, int Hkv, int D, float softmax_scale, void* stream) {
+  return fwd_impl(map, q, k, v, o, lse, nullptr, B, S, Hq, Hkv, D, softmax_scale, 0.f, stream);
+}
+
+int pba_packed_attn_fwd_rope(const pba_block_map* map, const void* q, const void* k_rot, const void* v, void* o,
+                             float* lse, void* q_rot, int B, int S, int Hq, int Hkv, int D, float softmax_scale,
+                             float rope_base, void* stream) {
+  if (!(rope_base > 1.f) || !std::isfinite(rope_base)) return PBA_ERR_ARG;
+  return fwd_impl(map, q, k_rot, v, o, lse, q_rot, B, S, Hq, Hkv, D, softmax_scale, rope_base, stream);
 }
 
 size_t pba_bwd_workspace_bytes(int B, int S, int Hq, int D) {

@@ -218,7 +218,7 @@ __device__ __forceinline__ void fwd_pv(f32x16 (&o)[D / 32], const bf16x8 (&p)[2]
   }
 }
 
-template <int D, int WGH>
+template <int D, int WGH, bool ROPE>
 __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   static_assert(C::KSTR == C::VSTR, "K and V tiles share one stager");
@@ -299,6 +299,38 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
     const char* qr = q_lds + (qb * 32 + l32) * Blk::LSTR + hw * D * 2 + 16 * hi;
 #pragma unroll
     for (int st = 0; st < C::NS; ++st) qop[st] = *(const bf16x8*)(qr + 32 * st);
+  }
+  if constexpr (ROPE) {
+    // Rotary embedding of Q at the query's packed position (pad: 0, the
+    // identity; a pad query's window starts after itself): head dim d pairs
+    // with d + D/2, i.e. qop[st] with qop[st + NS/2] in the same lane.
+    const int pos = wlo > qi ? 0 : (wphi - wplo) + (qi - wlo);
+    const float pr = (float)pos * 0.15915494309189535f;  // revolutions per unit frequency
+#pragma unroll
+    for (int st = 0; st < C::NS / 2; ++st) {
+      bf16x8 u = qop[st], v = qop[st + C::NS / 2];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int d = 16 * st + 8 * hi + j;
+        float rev = pr * exp2f(-(float)(2 * d) / (float)D * a.rope_log2_base);
+        rev -= floorf(rev);
+        const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+        const float x1 = (float)u[j], x2 = (float)v[j];
+        u[j] = (bf16)(x1 * cs - x2 * sn);
+        v[j] = (bf16)(x1 * sn + x2 * cs);
+      }
+      qop[st] = u;
+      qop[st + C::NS / 2] = v;
+    }
+    if (a.q_rot) {
+      // The rotated block leaves through LDS as whole rows for the backward.
+      char* qw = q_lds + (qb * 32 + l32) * Blk::LSTR + hw * D * 2 + 16 * hi;
+#pragma unroll
+      for (int st = 0; st < C::NS; ++st) *(bf16x8*)(qw + 32 * st) = qop[st];
+      __syncthreads();
+      Blk::template store<256>(a.q_rot + ((int64_t)b * S + q0) * Hq * D + (int64_t)h0 * D, q_lds, qrows, qrow_bytes,
+                               tid);
+    }
   }
 
   float m = kNegInf, l = 0.f, alpha = 1.f;
@@ -383,17 +415,17 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   Blk::template store<256>(a.o + ((int64_t)b * S + q0) * Hq * D + (int64_t)h0 * D, qo_lds, qrows, qrow_bytes, tid);
 }
 
-template <int D>
+template <int D, bool ROPE>
 hipError_t launch_fwd_d(const FwdArgs& a, int wgh, unsigned nblk, hipStream_t stream) {
   switch (wgh) {
     case 4:
-      hipLaunchKernelGGL((fwd_kernel<D, 4>), dim3(nblk), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<D, 4, ROPE>), dim3(nblk), dim3(256), 0, stream, a);
       break;
     case 2:
-      hipLaunchKernelGGL((fwd_kernel<D, 2>), dim3(nblk), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<D, 2, ROPE>), dim3(nblk), dim3(256), 0, stream, a);
       break;
     default:
-      hipLaunchKernelGGL((fwd_kernel<D, 1>), dim3(nblk), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<D, 1, ROPE>), dim3(nblk), dim3(256), 0, stream, a);
       break;
   }
   return hipGetLastError();
@@ -406,7 +438,9 @@ int fwd_wg_heads(int G) { return (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1); }
 hipError_t launch_fwd(const FwdArgs& a, int D, int B, hipStream_t stream) {
   const int wgh = fwd_wg_heads(a.G);
   const unsigned nblk = (unsigned)((int64_t)B * a.map.nqt * (a.Hq / wgh));
-  return D == 128 ? launch_fwd_d<128>(a, wgh, nblk, stream) : launch_fwd_d<64>(a, wgh, nblk, stream);
+  if (a.rope_log2_base != 0.f)
+    return D == 128 ? launch_fwd_d<128, true>(a, wgh, nblk, stream) : launch_fwd_d<64, true>(a, wgh, nblk, stream);
+  return D == 128 ? launch_fwd_d<128, false>(a, wgh, nblk, stream) : launch_fwd_d<64, false>(a, wgh, nblk, stream);
 }
 
 }  // namespace pba

@@ -45,6 +45,11 @@ struct FwdArgs {
   float* lse;
   int S, Hq, Hkv, G, wg_heads;
   float scale_log2;  // softmax scale * log2(e)
+  // Rotary inputs: Q is rotated at the packed positions inside the kernel
+  // (log2 of the base; 0 = Q is used as given) and, if q_rot is not null,
+  // written there for the backward.
+  float rope_log2_base;
+  bf16* q_rot;
 };
 
 struct BwdArgs {

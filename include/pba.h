@@ -312,6 +312,19 @@ PBA_API int pba_packed_attn_fwd(const pba_block_map* map, const void* q, const v
                         void* o, float* lse, int B, int S, int Hq, int Hkv, int D,
                         float softmax_scale, void* stream);
 
+/* Forward for rotary inputs, with the rotation of Q fused in: q is the
+ * UNROTATED Q, k_rot is K rotated by pba_packed_rope at the packed
+ * positions with the same base.  Each workgroup rotates its Q block in
+ * registers at the queries' packed positions before the scores (rotate-half
+ * pairing; angles reduced to revolutions in fp32 for the hardware sine and
+ * cosine) and, if q_rot is not NULL (bf16, Q's layout), also writes the
+ * rotated Q there, which is what pba_packed_attn_bwd_rope takes.  O and LSE
+ * as pba_packed_attn_fwd on the rotated inputs.  rope_base must be above 1
+ * and finite (PBA_ERR_ARG). */
+PBA_API int pba_packed_attn_fwd_rope(const pba_block_map* map, const void* q, const void* k_rot, const void* v,
+                                     void* o, float* lse, void* q_rot, int B, int S, int Hq, int Hkv, int D,
+                                     float softmax_scale, float rope_base, void* stream);
+
 /* Workspace bytes the backward needs: two fp32 [B, Hq, S] arrays (the row
  * dot products rowsum(dO * O) and the log2-domain LSE), written by the dQ
  * stage and read by the dK / dV stage; 0 on bad arguments. */

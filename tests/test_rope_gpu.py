@@ -16,11 +16,17 @@ from workloads.generate import descriptor_arrays, make_packset, random_packset
 pytestmark = pytest.mark.gpu
 
 
-def _bound_ok(x, y, yref):
+def _bound_ok(x, y, yref, rel=2.0 ** -8):
     D = x.shape[-1]
     xs = x.abs()
     pair = torch.cat([xs[..., : D // 2] + xs[..., D // 2:]] * 2, dim=-1)
-    return bool(((y - yref).abs() <= 2.0 ** -8 * yref.abs() + 3e-3 * pair).all())
+    return bool(((y - yref).abs() <= rel * yref.abs() + 3e-3 * pair).all())
+
+
+def _same_rotation(x, y1, y2):
+    """Two bf16 roundings of (nearly) the same rotation differ by at most one
+    bf16 ulp (2^-7 relative) plus the fp32 angle error of each."""
+    return _bound_ok(x, y1, y2, rel=2.0 ** -7)
 
 
 def _run(ps, H, D, base, seed, inverse=False, in_place=False):
@@ -135,17 +141,22 @@ def _rope_case(w, base):
     q, k, v, do = (x.cuda().contiguous() for x in (w.q, w.k, w.v, w.do))
     fm = build_map(ps, *A.fwd_tile(w.Hq, w.Hkv, w.D))
     bm = build_map(ps, *A.bwd_tile(w.Hq, w.Hkv, w.D))
-    qr, kr = A.packed_rope(fm, q, base), A.packed_rope(fm, k, base)
-    o, lse = A.packed_attn_fwd(fm, qr, kr, v, w.scale)
+    kr = A.packed_rope(fm, k, base)
+    # fused: Q rotated inside the forward (which also writes it), gradients
+    # rotated back inside the backward
+    o, lse, qr = A.packed_attn_fwd_rope(fm, q, kr, v, base, w.scale)
     dq, dk, dv = A.packed_attn_bwd_rope(fm, bm, qr, kr, v, o, lse, do, base, w.scale)
-    # the same through the unfused path: plain backward, then inverse rotation passes
-    dq_r, dk_r, dv_u = A.packed_attn_bwd(fm, bm, qr, kr, v, o, lse, do, w.scale)
+    # unfused: rotation passes around the plain forward and backward
+    qr_u = A.packed_rope(fm, q, base)
+    o_u, lse_u = A.packed_attn_fwd(fm, qr_u, kr, v, w.scale)
+    dq_r, dk_r, dv_u = A.packed_attn_bwd(fm, bm, qr_u, kr, v, o_u, lse_u, do, w.scale)
     dq_u, dk_u = A.packed_rope(fm, dq_r, base, inverse=True), A.packed_rope(fm, dk_r, base, inverse=True)
     torch.cuda.synchronize()
     P, Rl = descriptor_arrays(ps)
     pos = oracle.positions(P, Rl, ps.B, ps.S)[0]
-    return {"o": o.cpu(), "dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu(), "dq_u": dq_u.cpu(), "dk_u": dk_u.cpu(),
-            "dv_u": dv_u.cpu(), "pos": pos, "P": P, "R": Rl}
+    return {"o": o.cpu(), "dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu(), "o_u": o_u.cpu(), "dq_u": dq_u.cpu(),
+            "dk_u": dk_u.cpu(), "dv_u": dv_u.cpu(), "qr": qr.cpu(), "qr_u": qr_u.cpu(), "q": w.q, "pos": pos, "P": P,
+            "R": Rl}
 
 
 def _rel(x, ref):
@@ -166,7 +177,9 @@ def test_fused_rope_backward_tiny_vs_oracle():
     dqr, dkr, dv = oracle.attn_bwd(qr, kr, w.v, w.do, mask, w.scale)
     dq, dk = R.packed_rope(dqr, got["pos"], base, inverse=True), R.packed_rope(dkr, got["pos"], base, inverse=True)
     say("fused rope bwd tiny", _rel(got["dq"], dq), _rel(got["dk"], dk), _rel(got["dv"], dv))
-    assert _rel(got["o"], O) <= 1e-2
+    assert _rel(got["o"], O) <= 1e-2 and _rel(got["o_u"], O) <= 1e-2
+    # the forward's rotated Q equals the rotation pass's up to bf16 rounding
+    assert _same_rotation(got["q"].double(), got["qr"].double(), got["qr_u"].double())
     for name, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
         assert _rel(got[name], ref) <= 1e-2, name
         assert _rel(got[name + "_u"], ref) <= 1e-2, name + " unfused"
@@ -195,3 +208,8 @@ def test_fused_rope_backward_qwen3_packs_sampled():
     e = (_rel(dq, dq_ref), _rel(got["dk"][b, krows, g], dk_ref), _rel(got["dv"][b, krows, g], dvs))
     say("fused rope bwd qwen3 packs sampled", b, g, e)
     assert max(e) <= 1e-2, e
+    # forward: sampled rows of one head against the oracle on rotated inputs
+    h = g * G
+    Os, _ = oracle.attn_fwd_rows(qr, kr, w.v, mb, b, h, qrows, w.scale)
+    assert _rel(got["o"][b, qrows, h], Os) <= 1e-2
+    assert _same_rotation(got["q"].double(), got["qr"].double(), got["qr_u"].double())
