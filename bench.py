@@ -528,7 +528,8 @@ def main():
 
     # Rotary embedding at the packed positions (a step before attention, reported beside the step).
     extra["rope"] = rope_rate(A, torch, r, q, k)
-    extra["rope"]["attention_step"] = rope_step_cost(A, torch, r, q, k, v, do, w.scale)
+    if not args.no_baselines:
+        extra["rope"]["attention_step"] = rope_step_cost(A, torch, r, q, k, v, do, w.scale)
     log(f"rope: {json.dumps(extra['rope'])}")
 
     # Packed token log-probs over a Qwen3-sized vocabulary (a next step after attention, reported beside the step).
