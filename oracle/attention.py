@@ -101,6 +101,25 @@ def attn_fwd_rows(q, k, v, mask_b, b, h, qrows, scale):
     return P @ v[b, :, g], lse
 
 
+def attn_dq_rows(q, k, v, do, mask_rows, b, h, qrows, scale):
+    """dQ [n, D] of the listed query rows of (batch row b, q head h) for the
+    loss <dO, O>, each row from its own softmax: P_i, O_i = P_i V, the row dot
+    product Delta_i = dO_i . O_i, dS_ij = P_ij (dO_i . V_j - Delta_i) and
+    dQ_i = scale sum_j dS_ij K_j.  mask_rows [n, S] are those rows of the
+    mask (so that very long rows need no S x S mask)."""
+    q, k, v, do = _t(q), _t(k), _t(v), _t(do)
+    G = q.shape[2] // k.shape[2]
+    g = h // G
+    idx = torch.as_tensor(np.asarray(qrows), dtype=torch.long)
+    m = torch.from_numpy(np.ascontiguousarray(mask_rows))
+    P, _ = _probs(q[b, idx, h], k[b, :, g], m, scale)
+    O = P @ v[b, :, g]
+    dOi = do[b, idx, h]
+    delta = (dOi * O).sum(dim=1)
+    dS = P * (dOi @ v[b, :, g].T - delta[:, None])
+    return scale * (dS @ k[b, :, g])
+
+
 def attn_bwd_sampled(q, k, v, do, mask_b, b, g, qrows, krows, scale):
     """Gradients at sampled positions of batch row b and kv group g:
     dQ[qrows] for every q head of the group ([G, n, D]) and dK[krows],

@@ -94,6 +94,19 @@ def attention_mask(tok_pack, tok_branch, row=None):
     return m if row is None else m[0]
 
 
+def attention_mask_rows(tok_pack, tok_branch, row, queries):
+    """allowed[i, j] of batch row `row` for the listed query positions only
+    (the same rule as attention_mask, without forming the S x S matrix)."""
+    pk, br = tok_pack[row], tok_branch[row]
+    q = np.asarray(queries)
+    S = pk.shape[0]
+    j = np.arange(S)[None, :]
+    same_pack = (pk[None, :] == pk[q][:, None]) & (pk[q][:, None] >= 0)
+    causal = j <= q[:, None]
+    branch_ok = (br[None, :] == 0) | (br[None, :] == br[q][:, None])
+    return same_pack & causal & branch_ok
+
+
 def allowed_count(mask) -> int:
     return int(np.count_nonzero(mask))
 

@@ -255,3 +255,38 @@ def test_sampled_equals_full():
     dqs, dks, dvs = oracle.attn_bwd_sampled(w.q, w.k, w.v, w.do, m[0], 0, 1, rows, [2, 30], w.scale)
     assert torch.allclose(dqs, torch.stack([dq[0, rows, 2], dq[0, rows, 3]]), atol=1e-14)
     assert torch.allclose(dks, dk[0, [2, 30], 1], atol=1e-14) and torch.allclose(dvs, dv[0, [2, 30], 1], atol=1e-14)
+
+
+def test_mask_rows_match_the_full_mask():
+    rng = np.random.default_rng(8)
+    for _ in range(10):
+        pl = [(0, 0, int(rng.integers(0, 6)), tuple(int(x) for x in rng.integers(0, 5, size=int(rng.integers(0, 4))))),
+              (0, 20, int(rng.integers(0, 4)), (int(rng.integers(1, 4)),))]
+        P, R = descriptors(pl)
+        pk, br, _ = oracle.token_ids(P, R, 1, 30)
+        full = oracle.attention_mask(pk, br, row=0)
+        rows = rng.choice(30, size=7, replace=False)
+        assert np.array_equal(oracle.attention_mask_rows(pk, br, 0, rows), full[rows])
+
+
+def test_dq_rows_by_finite_differences():
+    """attn_dq_rows is the gradient of <dO, O> with respect to the listed
+    query rows (central differences on those rows), and it equals the full
+    backward's rows."""
+    pl = [(0, 0, 4, (3, 5)), (0, 12, 2, (2,)), (0, 17, 0, (3,))]
+    S, Hq, Hkv, D, scale = 22, 4, 2, 8, 0.37
+    m = _mask(1, S, pl)
+    q, k, v, do = _rand((1, S, Hq, D), 61), _rand((1, S, Hkv, D), 62), _rand((1, S, Hkv, D), 63), _rand((1, S, Hq, D), 64)
+    rows = [0, 3, 7, 8, 13, 16, 19, 21]
+    h = 3
+    dq_rows = oracle.attn_dq_rows(q, k, v, do, m[0][rows], 0, h, rows, scale)
+    dq, _, _ = oracle.attn_bwd(q, k, v, do, m, scale)
+    assert torch.allclose(dq_rows, dq[0, rows, h], atol=1e-13, rtol=0)
+    eps = 1e-6
+    for n, i in enumerate(rows):
+        for d in (0, 5):
+            qp, qm = q.clone(), q.clone()
+            qp[0, i, h, d] += eps
+            qm[0, i, h, d] -= eps
+            num = (_loss(qp, k, v, do, m, scale) - _loss(qm, k, v, do, m, scale)) / (2 * eps)
+            assert abs(num - float(dq_rows[n, d])) <= 1e-7 * max(1.0, abs(num))
