@@ -1,0 +1,99 @@
+"""One very long pack (131 072 tokens: a 65 536-token prompt and two
+32 768-token responses; 32/8 heads, D = 128): the largest single-row case
+the library's 2 GiB-per-row limit allows at this width, far past the
+workloads' 9 428 tokens.
+
+Checked against the oracle where it can compute one row at a time
+(forward rows, dQ rows: each needs only that row's keys), and through
+properties that hold at any size for dK and dV (with P's rows summing to 1:
+sum_j dV_j = sum_i dO_i over each kv group's q heads, and sum_j dK_j = 0
+because each row of dS sums to 0).  Tolerances: O and LSE as for the
+workloads on every checked row; dQ rel-L2 1e-2 over uniformly drawn rows
+(an estimate of the whole tensor's), and per row 2e-2 on the boundary rows
+(rows that see only two or three keys carry the largest relative error:
+their dS is a difference of two nearly equal terms, Delta coming from the
+bf16 O); the dV sum to rel 1e-2; the dK sum must be far below the
+root-sum-square of the dK rows (a sum of 131 072 independently rounded terms
+lands near 2^-9 of it; 0.05 leaves 25x margin, while a missing or
+mis-scaled term lands near 1)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_path import api, say
+from workloads.generate import Pack, PackSet, descriptor_arrays
+
+pytestmark = pytest.mark.gpu
+
+
+class _Rows:
+    """Mask lookup that returns precomputed rows (attn_fwd_rows indexes the
+    mask by the query rows it is given)."""
+
+    def __init__(self, rows_mask):
+        self.m = rows_mask
+
+    def __getitem__(self, idx):
+        return self.m
+
+
+def _rel(x, ref):
+    x, ref = x.double(), ref.double()
+    return float((x - ref).norm() / ref.norm())
+
+
+def test_one_pack_of_131072_tokens():
+    A = api()
+    p, r1, r2 = 65536, 32768, 32768
+    S, Hq, Hkv, D = p + r1 + r2, 32, 8, 128
+    ps = PackSet(1, S, [Pack(0, 0, p, (r1, r2))])
+    scale = 1.0 / D ** 0.5
+    g = torch.Generator(device="cuda").manual_seed(2026)
+    q = (torch.randn((1, S, Hq, D), generator=g, device="cuda") * scale).to(torch.bfloat16)
+    k = (torch.randn((1, S, Hkv, D), generator=g, device="cuda") * scale).to(torch.bfloat16)
+    v = (torch.randn((1, S, Hkv, D), generator=g, device="cuda") * scale).to(torch.bfloat16)
+    do = torch.randn((1, S, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+    P, R = descriptor_arrays(ps)
+    pd, rd = A.descriptors_to_device(P, R)
+    fm = A.pack_block_map(pd, rd, 1, S, *A.fwd_tile(Hq, Hkv, D))
+    bm = A.pack_block_map(pd, rd, 1, S, *A.bwd_tile(Hq, Hkv, D))
+    say("long pack: map built", S)
+    o, lse = A.packed_attn_fwd(fm, q, k, v, scale)
+    dq, dk, dv = A.packed_attn_bwd(fm, bm, q, k, v, o, lse, do, scale)
+    torch.cuda.synchronize()
+    say("long pack: fwd + bwd done")
+    assert fm.status().cpu().tolist() == [0, -1] and bm.status().cpu().tolist() == [0, -1]
+
+    pk, br, _ = oracle.token_ids(P, R, 1, S)
+    edge = np.array([0, 1, 2, 4095, p - 1, p, p + 1, p + r1 - 1, p + r1, p + r1 + 7, S - 1])
+    drawn = np.sort(np.random.default_rng(3).choice(S, size=24, replace=False))
+    rows = np.concatenate([edge, drawn])
+    mrows = oracle.attention_mask_rows(pk, br, 0, rows)
+    n = len(rows)
+    ne = len(edge)
+    for h in (0, 13, 31):
+        gk = h // (Hq // Hkv)
+        qs = q[:, rows, h:h + 1].cpu()
+        ks, vs = k[:, :, gk:gk + 1].cpu(), v[:, :, gk:gk + 1].cpu()
+        dos = do[:, rows, h:h + 1].cpu()
+        O, L = oracle.attn_fwd_rows(qs, ks, vs, _Rows(mrows), 0, 0, np.arange(n), scale)
+        got_o = o[0, rows, h].cpu().double()
+        assert float((got_o - O).abs().max()) <= 1e-2 and _rel(got_o, O) <= 1e-2, h
+        assert float((lse[0, h, rows].cpu().double() - L).abs().max()) <= 1e-3, h
+        dQ = oracle.attn_dq_rows(qs, ks, vs, dos, mrows, 0, 0, np.arange(n), scale)
+        got_dq = dq[0, rows, h].cpu().double()
+        e = _rel(got_dq[ne:], dQ[ne:])
+        say("  head", h, "dq rel-L2 on drawn rows", e)
+        assert e <= 1e-2, (h, e)
+        err = (got_dq[:ne] - dQ[:ne]).norm(dim=1)
+        assert bool((err <= 2e-2 * dQ[:ne].norm(dim=1) + 1e-6).all()), (h, err.tolist())
+
+    G = Hq // Hkv
+    for gk in range(Hkv):
+        sum_dv = dv[0, :, gk].float().sum(0).double().cpu()
+        sum_do = do[0, :, gk * G:(gk + 1) * G].float().sum((0, 1)).double().cpu()
+        assert _rel(sum_dv, sum_do) <= 1e-2, gk
+        dkg = dk[0, :, gk].float()
+        rss = float(dkg.pow(2).sum().sqrt())
+        assert float(dkg.sum(0).norm()) <= 0.05 * rss, gk
