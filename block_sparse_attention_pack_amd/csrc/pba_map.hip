@@ -284,11 +284,11 @@ __global__ void __launch_bounds__(kThreads) map_lists(MapSet ms) {
 
 // Work order of one side of one map: the tiles sorted by visit count
 // (n_full + n_partial), descending, ties by index ascending.  Up to
-// kOrderLds tiles: counts in LDS and each tile's position is its rank,
-// #{j : c_j > c_i} + #{j < i : c_j = c_i}, one pass over the counts per
-// tile (LDS broadcast reads).  Beyond that: a stable counting sort through
-// the map's work area (histogram, scan from the largest count down, then
-// placement one chunk at a time), accessed with device-scope atomics only.
+// kOrderLds tiles: a bitonic sort in LDS of unique keys that encode both
+// (so the result is the same as a stable sort).  Beyond that: a stable
+// counting sort through the map's work area (histogram, scan from the
+// largest count down, then placement one chunk at a time), accessed with
+// device-scope atomics only.
 __global__ void __launch_bounds__(kOrderThreads) map_order(MapSet ms) {
   const MapOut& m = ms.m[blockIdx.y];
   if (m.status[0] != 0) return;
