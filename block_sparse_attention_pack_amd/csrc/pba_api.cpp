@@ -44,7 +44,7 @@ MapLayout map_layout(int B, int S, int bm, int bn) {
       2 * 4,                  // status
       4 * (size_t)B * nqt,    // q_order
       4 * (size_t)B * nkt,    // k_order
-      4 * (nqt + nkt + 2),    // work (order histograms)
+      4 * (nqt + nkt + 4),    // work (order histograms, arrival counters)
   };
   MapLayout L;
   size_t o = 0;

@@ -181,7 +181,8 @@ PBA_API int pba_pack_block_map(const pba_pack* packs, int n_packs, const int32_t
 
 /* The same for n_maps maps of the same rows (same B and S, any tile shapes;
  * `maps` is a host array of n_maps initialised maps, 1 <= n_maps <=
- * PBA_MAX_MAPS_PER_BUILD), built together in four launches: the forward /
+ * PBA_MAX_MAPS_PER_BUILD), built together in two launches (three when one side
+ * of a map has more than 2048 tiles): the forward /
  * dQ map and the dK / dV map of a batch are built with one call.  Each map
  * ends up exactly as pba_pack_block_map would build it. */
 #define PBA_MAX_MAPS_PER_BUILD 4
