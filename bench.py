@@ -150,6 +150,62 @@ def traffic_record(kernel):
     return rec
 
 
+TRAFFIC_KERNELS = {  # record name -> (kernel name prefix in rocprofv3 output, source files)
+    "fwd": ("fwd_kernel<128, 4, false>", ["pba_fwd.hip", "pba_tile.h", "pba_internal.h"]),
+    "bwd_dq": ("bwd_dq<128, 4>", ["pba_bwd.hip", "pba_tile.h", "pba_internal.h"]),
+    "bwd_dkdv": ("bwd_dkdv<128>", ["pba_bwd.hip", "pba_tile.h", "pba_internal.h"]),
+}
+
+
+def write_traffic(fetch_csv, write_csv, workload):
+    """profiles/traffic_<kernel>.json from two rocprofv3 --pmc runs of
+    `bench.py --copy-calibration` (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch), each scaled by what the same counter reads for the plain
+    2^28-byte device copy (2^28 bytes read and written per launch)."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row["Kernel_Name"]
+                # The calibration copy is the only copy dispatch of 2^28 bytes
+                # (its grid is far larger than the small descriptor copies').
+                if "copyBuffer" in name:
+                    if int(row["Grid_Size"]) < 65536:
+                        continue
+                    name = "calibration copyBuffer"
+                vals.setdefault(name, []).append(float(row["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+
+    def avg(vals, prefix):
+        xs = [x for name, v in vals.items() if prefix in name for x in v]
+        if not xs:
+            raise SystemExit(f"no {prefix} dispatches in the counter output")
+        return sum(xs) / len(xs), len(xs)
+
+    copy_kib = float(1 << 28) / 1024
+    fetch_scale = copy_kib / avg(fetch, "calibration copyBuffer")[0]
+    write_scale = copy_kib / avg(write, "calibration copyBuffer")[0]
+    for rec_name, (prefix, sources) in TRAFFIC_KERNELS.items():
+        fk, n = avg(fetch, prefix)
+        wk, _ = avg(write, prefix)
+        rec = {"kernel": rec_name, "workload": workload, "sources": sources,
+               "sources_sha256": sources_sha256(sources), "dispatches": n,
+               "fetch_kib_raw": fk, "write_kib_raw": wk, "fetch_scale": fetch_scale, "write_scale": write_scale,
+               "read_bytes_per_launch": fk * fetch_scale * 1024, "write_bytes_per_launch": wk * write_scale * 1024}
+        rec["hbm_bytes_per_launch"] = rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"]
+        with open(os.path.join(ROOT, "profiles", f"traffic_{rec_name}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        log(f"{rec_name}: read {rec['read_bytes_per_launch'] / 1e6:.1f} MB, write "
+            f"{rec['write_bytes_per_launch'] / 1e6:.1f} MB per launch ({n} dispatches); "
+            f"scales {fetch_scale:.4f} / {write_scale:.4f}")
+
+
 def measured_mfma_peak(A, torch):
     """Sustained bf16 MFMA rate of this device: the library's probe loop
     (independent accumulators, every CU busy), in TFLOP/s."""
@@ -436,7 +492,13 @@ def main():
     ap.add_argument("--no-baselines", action="store_true", help="skip the dense-map and pairwise-layout runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_*.json from two rocprofv3 counter_collection.csv files "
+                         "(FETCH_SIZE run, WRITE_SIZE run) and exit; uses no GPU")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic, workload="qwen3_8b_packs (8 x 1828 tokens, 32/8 heads, D=128)")
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path (packs and kv-head groups "

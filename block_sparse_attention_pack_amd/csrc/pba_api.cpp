@@ -3,6 +3,7 @@
 // stream.  Descriptor contents are checked on the device by the map kernels.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -78,7 +79,7 @@ int device_ok() {
 
 int check_map(const pba_block_map* m, int B, int S, int bm, int bn) {
   if (!m || !m->tok_win || !m->q2k_cnt || !m->q2k_idx || !m->k2q_cnt || !m->k2q_idx || !m->status || !m->q_order ||
-      !m->k_order)
+      !m->k_order || !m->totals)
     return PBA_ERR_NULL;
   if (m->B != B || m->S != S) return PBA_ERR_MAP;
   if (m->block_m != bm || m->block_n != bn) return PBA_ERR_TILE;
@@ -91,6 +92,28 @@ int check_heads(int B, int S, int Hq, int Hkv, int D) {
   if (Hq % Hkv != 0) return PBA_ERR_HEADS;
   if (D != 64 && D != 128) return PBA_ERR_HEAD_DIM;
   return PBA_OK;
+}
+
+// Split key tiles of bwd_dkdv: at most this many (position, kv group)
+// pairs have a partial-sum area in the workspace.
+size_t split_pairs(int B, int S, int Hq) {
+  const size_t nkt = (size_t)((S + pba::kBwdBN - 1) / pba::kBwdBN);
+  return std::min((size_t)pba::kMaxSplitPairs, (size_t)B * nkt * Hq);
+}
+
+// Compute units of the current device, cached per device (0 if unknown).
+int cu_count() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lk(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 // The softmax is evaluated as exp2(s * scale * log2(e) - m) with the row
@@ -110,7 +133,7 @@ pba::MapView view_of(const pba_block_map* m) {
   v.B = m->B; v.S = m->S; v.bm = m->block_m; v.bn = m->block_n; v.nqt = m->nqt; v.nkt = m->nkt;
   v.tok_win = m->tok_win; v.q2k_cnt = m->q2k_cnt; v.q2k_idx = m->q2k_idx;
   v.k2q_cnt = m->k2q_cnt; v.k2q_idx = m->k2q_idx; v.status = m->status;
-  v.q_order = m->q_order; v.k_order = m->k_order;
+  v.q_order = m->q_order; v.k_order = m->k_order; v.totals = m->totals;
   return v;
 }
 
@@ -388,7 +411,8 @@ int pba_packed_attn_fwd_rope(const pba_block_map* map, const void* q, const void
 
 size_t pba_bwd_workspace_bytes(int B, int S, int Hq, int D) {
   if (B < 1 || B > kMaxB || S < 1 || S > kMaxS || Hq < 1 || Hq > kMaxHeads || (D != 64 && D != 128)) return 0;
-  return 2 * align_up((size_t)B * Hq * S * 4);
+  const size_t pairs = split_pairs(B, S, Hq);
+  return 2 * align_up((size_t)B * Hq * S * 4) + align_up((pairs + 1) * 4) + pairs * 2 * 2 * pba::kBwdBN * D * 4;
 }
 
 }  // extern "C"
@@ -437,6 +461,13 @@ int bwd_impl(int stages, const pba_block_map* qmap, const pba_block_map* kmap, c
   a.scale = softmax_scale;
   a.scale_log2 = softmax_scale * pba::kLog2eHost;
   a.rope_log2_base = rope_base > 0.f ? std::log2(rope_base) : 0.f;
+  // Split area: arrival counters, then the partial sums.
+  const size_t pairs = split_pairs(B, S, Hq);
+  char* split_base = static_cast<char*>(workspace) + 2 * align_up((size_t)B * Hq * S * 4);
+  a.arrive = reinterpret_cast<int32_t*>(split_base);
+  a.part = reinterpret_cast<float*>(split_base + align_up((pairs + 1) * 4));
+  a.slots = std::max(1, cu_count() / Hkv);
+  a.nsplit = (int)std::min({(size_t)B * kmap->nkt, (size_t)a.slots, pairs / (size_t)Hkv});
   hipError_t e = pba::launch_bwd(a, D, stages, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PBA_OK : PBA_ERR_DEVICE;
 }

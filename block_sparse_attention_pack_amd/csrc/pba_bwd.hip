@@ -22,6 +22,10 @@
 //             tiles and, for each q head of the group, S = Q K^T, dP = dO V^T,
 //             dV^T += dO^T P, dK^T += Q^T dS, summing over the group's heads;
 //             the two query halves' partial sums meet in LDS at the end.
+//             Key tiles with a list longer than the average load of one
+//             workgroup slot (the prompt tiles of a pack shared by many
+//             responses) are split between two workgroups, whose fp32 sums
+//             meet in the workspace: the second to finish adds them.
 //
 // dQ and dK / dV are each owned by exactly one workgroup, so they are written
 // once, in bf16, with no accumulator pass (fp32 atomics into a dQ buffer are
@@ -144,6 +148,24 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   asm volatile("" ::"s"(map_status), "s"(order_entry), "s"(mp.q2k_cnt), "s"(mp.q2k_idx));
   if (map_status != 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
+  // Workgroup 0 prepares bwd_dkdv's split key tiles: the arrival counters
+  // start at zero, and the number of leading work-order positions whose
+  // list is longer than the average load of a workgroup slot (all visited
+  // tiles of the key-major map over the slots of one kv group) is stored
+  // after them.  The work order is longest first, so those positions are a
+  // prefix of it.
+  if (blockIdx.x == 0) {
+    for (int i = tid; i < a.nsplit * a.Hkv; i += 256) a.arrive[i] = 0;
+    bool split = false;
+    if (tid < a.nsplit) {
+      const MapView& km = a.kmap;
+      const int it = min(max(km.k_order[tid], 0), km.B * km.nkt - 1);
+      const int n = min(max(km.k2q_cnt[2 * it] + km.k2q_cnt[2 * it + 1], 0), km.nqt);
+      split = (int64_t)n * a.slots > km.totals[0] + km.totals[1];
+    }
+    const int nsp = __syncthreads_count(split);
+    if (tid == 0) a.arrive[a.nsplit * a.Hkv] = nsp;
+  }
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int nhg = a.Hq / WGH;
@@ -365,13 +387,10 @@ __device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D
 }
 
 // End of bwd_dkdv: the wave of query half 1 puts its partial sums in its
-// lane-private LDS slot, the partner wave (half 0) adds them to its own and
-// writes scale * sum as bf16 into the row block `rows` (LDS, row = the
-// lane's key within the workgroup, LSTR bytes apart; lane: head dims
-// 32e + 8*(r/4) + 4*hi + r%4), from which the workgroup stores whole rows.
-template <int D, int LSTR>
-__device__ __forceinline__ void pair_sum_lds(const f32x16 (&acc)[D / 32], float* slot, int qh, char* rows, int krow,
-                                             int hi, float scale, bool rope, int pos, float log2_base) {
+// lane-private LDS slot and the partner wave (half 0) adds them to its own
+// (lane: key kj, head dims 32e + 8*(r/4) + 4*hi + r%4).
+template <int D>
+__device__ __forceinline__ void pair_add(f32x16 (&acc)[D / 32], float* slot, int qh) {
   constexpr int NE = D / 32;
   if (qh == 1) {
 #pragma unroll
@@ -383,31 +402,64 @@ __device__ __forceinline__ void pair_sum_lds(const f32x16 (&acc)[D / 32], float*
   }
   __syncthreads();
   if (qh == 0) {
-    f32x16 sum[NE];
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
+    for (int e = 0; e < NE; ++e)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const f32x4 o = *(const f32x4*)(slot + 16 * e + 4 * rg);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) sum[e][4 * rg + t] = acc[e][4 * rg + t] + o[t];
+        for (int t = 0; t < 4; ++t) acc[e][4 * rg + t] += o[t];
       }
-    }
-    // With rotary inputs, dK is rotated back at the key's packed position.
-    if (rope) rope_rotate_t<NE>(sum, pos, hi, log2_base, -1.f);
-    char* row = rows + krow * LSTR + 8 * hi;
-#pragma unroll
-    for (int e = 0; e < NE; ++e) {
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        bf16x4 v;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) v[t] = (bf16)(sum[e][4 * rg + t] * scale);
-        *(bf16x4*)(row + 2 * (32 * e + 8 * rg)) = v;
-      }
-    }
   }
   __syncthreads();
+}
+
+// The summed block (waves of query half 0) as scale * sum in bf16 into the
+// row block `rows` (LDS, row = the lane's key within the workgroup, LSTR
+// bytes apart), from which the workgroup stores whole rows; with rotary
+// inputs dK is first rotated back at the key's packed position.
+template <int D, int LSTR>
+__device__ __forceinline__ void rows_out(f32x16 (&sum)[D / 32], int qh, char* rows, int krow, int hi, float scale,
+                                         bool rope, int pos, float log2_base) {
+  constexpr int NE = D / 32;
+  if (qh != 0) return;
+  if (rope) rope_rotate_t<NE>(sum, pos, hi, log2_base, -1.f);
+  char* row = rows + krow * LSTR + 8 * hi;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      bf16x4 v;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[t] = (bf16)(sum[e][4 * rg + t] * scale);
+      *(bf16x4*)(row + 2 * (32 * e + 8 * rg)) = v;
+    }
+  }
+}
+
+// Partial sums of one (key block, lane) in the split area: D/8 chunks of
+// four floats, chunk c of lane l at (c * 64 + l) * 4 (whole 1 KB rows per
+// store instruction).
+template <int D>
+__device__ __forceinline__ void part_store(float* p, const f32x16 (&acc)[D / 32], int lane) {
+#pragma unroll
+  for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+      *(f32x4*)(p + ((4 * e + rg) * 64 + lane) * 4) =
+          f32x4{acc[e][4 * rg], acc[e][4 * rg + 1], acc[e][4 * rg + 2], acc[e][4 * rg + 3]};
+}
+
+template <int D>
+__device__ __forceinline__ void part_add(f32x16 (&acc)[D / 32], const float* p, int lane) {
+#pragma unroll
+  for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const f32x4 o = *(const f32x4*)(p + ((4 * e + rg) * 64 + lane) * 4);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[e][4 * rg + t] += o[t];
+    }
 }
 
 // 8 waves, 128 keys: wave w owns keys 32*(w%4) .. +31 and the query half
@@ -429,6 +481,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16 sDO[2][TQ];
   static_assert(2 * TQ * sizeof(bf16) >= 2 * 64 * (D / 2 + 4) * sizeof(float), "exchange must fit a staging array");
   __shared__ __attribute__((aligned(16))) float sL[2][64], sD[2][64];
+  __shared__ int s_second;  // this workgroup is the second half of a split key tile to finish
 
   const MapView& mp = a.kmap;
   if (cptr(mp.status)[0] != 0) return;
@@ -437,8 +490,22 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   const int l32 = lane & 31;
   const int kb = w & 3, qh = w >> 2;  // key block, query half
   const int Hkv = a.Hkv, G = a.G, S = a.S, Hq = a.Hq;
-  const int item = cptr(mp.k_order)[blockIdx.x / Hkv];
+  // Workgroup slots: with K split positions (counted by bwd_dq), the first
+  // 2K slots take the two halves of the first K work-order positions, the
+  // next ones one position each, and the nsplit - K slots at the end of the
+  // grid have nothing to do.
+  const int nsp = min(max(cptr(a.arrive)[a.nsplit * Hkv], 0), a.nsplit);
+  const int wslot = blockIdx.x / Hkv;
   const int g = blockIdx.x % Hkv;
+  if (wslot >= mp.B * mp.nkt + nsp) return;
+  int pos, half = -1;
+  if (wslot < 2 * nsp) {
+    pos = wslot >> 1;
+    half = wslot & 1;
+  } else {
+    pos = wslot - nsp;
+  }
+  const int item = min(max(cptr(mp.k_order)[pos], 0), mp.B * mp.nkt - 1);
   const int b = item / mp.nkt, kt = item % mp.nkt;
   const int kj = kt * 128 + 32 * kb + l32;  // this lane's key
   const int4 kwin = reinterpret_cast<const int4*>(mp.tok_win)[(int64_t)b * S + min(kj, S - 1)];
@@ -449,6 +516,13 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   const int n = min(max(cnt[0] + cnt[1], 0), mp.nqt);
   const int nfull = min(max(cnt[0], 0), n);
   const cint_ptr list = cptr(mp.k2q_idx) + lrow * mp.nqt;
+  // A split key tile: each half of its list goes to one workgroup.
+  int i0 = 0, i1 = n;
+  if (half >= 0) {
+    const int n0 = (n + 1) >> 1;
+    i0 = half ? n0 : 0;
+    i1 = half ? n : n0;
+  }
 
   const int kvstride = Hkv * D, qstride = Hq * D;
   const Stager<D, C::STR, 128, 8> kst(tid, kvstride);  // K and V
@@ -480,7 +554,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   // every outstanding global->LDS load, i.e. for the next step's tiles).
   const bf16* skp = opaque_lds(sK);
   const bf16* svp = opaque_lds(sV);
-  if (n > 0) stage(0, 0, 0);
+  if (i1 > i0) stage(i0, 0, 0);
   wait_vmem();
   __syncthreads();
   int buf = 0;
@@ -492,7 +566,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
     for (int hh = 0; hh < G; ++hh) {
       // Prefetch the next step into the other buffer (last read one step ago).
       if (hh + 1 < G) stage(i, hh + 1, buf ^ 1);
-      else if (i + 1 < n) stage(i + 1, 0, buf ^ 1);
+      else if (i + 1 < i1) stage(i + 1, 0, buf ^ 1);
       dkdv_step<D, decltype(masked)::value>(dkt, dvt, skp, svp, 32 * kb, sQ[buf], sDO[buf], sL[buf], sD[buf], 32 * qh,
                                             a.scale_log2, qrel, qlim, lane);
       wait_vmem();
@@ -500,14 +574,15 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
       buf ^= 1;
     }
   };
-  int i = 0;
-  for (; i < nfull; ++i) visit(i, std::false_type{});
-  for (; i < n; ++i) visit(i, std::true_type{});
+  int i = i0;
+  for (; i < min(nfull, i1); ++i) visit(i, std::false_type{});
+  for (; i < i1; ++i) visit(i, std::true_type{});
 
   // Sum the two query halves: the waves of half 1 hand their partial dK^T,
   // then dV^T, to their partners through LDS (lane-private slots in the
-  // Q / dO staging area), which write the result.  Lane: key kj, head dims
-  // 32e + 8*(r/4) + 4*hi + r%4.
+  // Q / dO staging area); for a split key tile the two workgroups' sums then
+  // meet in the workspace; the waves of half 0 write the result.  Lane: key
+  // kj, head dims 32e + 8*(r/4) + 4*hi + r%4.
   float* xch = reinterpret_cast<float*>(kb < 2 ? &sQ[0][0] : &sDO[0][0]);
   const int hi = lane >> 5;
   // Slots D/2 + 4 floats apart: 16 consecutive lanes start on 16 distinct
@@ -518,9 +593,44 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   using Blk = RowBlock<128, D * 2>;
   static_assert(128 * Blk::LSTR <= 128 * C::STR * 2, "a dK / dV block fits the K / V area");
   const int kpos = (kwin.z - kwin.y) + (kj - kwin.x);  // the key's packed position (rows past S are not stored)
-  pair_sum_lds<D, Blk::LSTR>(dkt, slot, qh, (char*)sK, 32 * kb + l32, hi, a.scale, a.rope_log2_base != 0.f, kpos,
-                             a.rope_log2_base);
-  pair_sum_lds<D, Blk::LSTR>(dvt, slot, qh, (char*)sV, 32 * kb + l32, hi, 1.f, false, 0, 0.f);
+  pair_add<D>(dkt, slot, qh);
+  pair_add<D>(dvt, slot, qh);
+  if (half >= 0) {
+    // The two workgroups of a split key tile: each leaves its fp32 sums in
+    // its own half of the pair's area; the second to arrive adds the
+    // other's (a + b = b + a, so the result does not depend on the order)
+    // and writes dK and dV.  Each wave waits for its own stores, then one
+    // agent-scope release publishes the block's stores before the counter
+    // moves; the second arriver acquires before reading.
+    const int64_t pair = (int64_t)pos * Hkv + g;
+    float* mine = a.part + ((pair * 2 + half) * 2) * (128 * D);
+    const float* other = a.part + ((pair * 2 + (half ^ 1)) * 2) * (128 * D);
+    if (qh == 0) {
+      part_store<D>(mine + kb * (32 * D), dkt, lane);
+      part_store<D>(mine + 128 * D + kb * (32 * D), dvt, lane);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const int old = __hip_atomic_fetch_add(a.arrive + pair, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_second = old == 1;
+      if (old == 1) {
+        __hip_atomic_store(a.arrive + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      }
+    }
+    __syncthreads();
+    if (!s_second) return;
+    if (qh == 0) {
+      part_add<D>(dkt, other + kb * (32 * D), lane);
+      part_add<D>(dvt, other + 128 * D + kb * (32 * D), lane);
+    }
+  }
+  rows_out<D, Blk::LSTR>(dkt, qh, (char*)sK, 32 * kb + l32, hi, a.scale, a.rope_log2_base != 0.f, kpos,
+                         a.rope_log2_base);
+  rows_out<D, Blk::LSTR>(dvt, qh, (char*)sV, 32 * kb + l32, hi, 1.f, false, 0, 0.f);
+  __syncthreads();
   const int krows = min(128, S - kt * 128);
   const int64_t out = ((int64_t)b * S + kt * 128) * kvstride + (int64_t)g * D;
   Blk::template store<512>(a.dk + out, (const char*)sK, krows, kvstride * 2, tid);
@@ -537,7 +647,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, int stages, hipStream_t stream) {
     else bwd_dq<D, 1><<<nblk, 256, 0, stream>>>(a);
   }
   if (stages & kBwdDkdv) {
-    const unsigned nblk = (unsigned)((int64_t)a.B * a.kmap.nkt * a.Hkv);
+    const unsigned nblk = (unsigned)(((int64_t)a.B * a.kmap.nkt + a.nsplit) * a.Hkv);
     bwd_dkdv<D><<<nblk, 512, 0, stream>>>(a);
   }
   return hipGetLastError();

@@ -34,6 +34,7 @@ struct MapView {  // device-side view of a pba_block_map
   const int32_t* status;
   const int32_t* q_order;  // [B*nqt] query tiles, longest visit list first
   const int32_t* k_order;  // [B*nkt] key tiles, longest visit list first
+  const int64_t* totals;   // [3] full, partial, skipped tiles
 };
 
 struct FwdArgs {
@@ -72,7 +73,21 @@ struct BwdArgs {
   // unrotated Q and K (the inputs were rotated at the packed positions);
   // 0 = no rotation.
   float rope_log2_base;
+  // Key tiles whose visit list is longer than the average load of one
+  // workgroup slot are split between two workgroups (bwd_dkdv): the first
+  // nsplit work-order positions may be split; their halves' fp32 partial
+  // sums meet in `part` ([nsplit*Hkv][2 halves][2 tensors][4 key blocks]
+  // [D/8][64 lanes] x 4 floats), counted in `arrive` ([nsplit*Hkv], zeroed
+  // by bwd_dq, followed by the number of positions actually split, also
+  // written by bwd_dq).  slots = workgroup slots per kv group (CUs / Hkv,
+  // >= 1).
+  float* part;
+  int32_t* arrive;
+  int nsplit, slots;
 };
+
+// Upper bound on nsplit * Hkv (sizes the split area of the workspace).
+constexpr int kMaxSplitPairs = 256;
 
 constexpr float kLog2eHost = 1.4426950408889634f;
 

@@ -328,7 +328,12 @@ PBA_API int pba_packed_attn_fwd_rope(const pba_block_map* map, const void* q, co
 
 /* Workspace bytes the backward needs: two fp32 [B, Hq, S] arrays (the row
  * dot products rowsum(dO * O) and the log2-domain LSE), written by the dQ
- * stage and read by the dK / dV stage; 0 on bad arguments. */
+ * stage and read by the dK / dV stage, then the area of the dK / dV stage's
+ * split key tiles (a key tile whose visit list is longer than the average
+ * load of one workgroup slot is shared by two workgroups): arrival counters
+ * and fp32 partial sums for at most min(256, B * ceil(S / 128) * Hq)
+ * (key tile, kv head) pairs, 256 KB each at D = 128 (64 MB at most); 0 on
+ * bad arguments. */
 PBA_API size_t pba_bwd_workspace_bytes(int B, int S, int Hq, int D);
 
 /* Backward of the forward above for the loss <dO, O>: dQ, dK, dV (bf16),
@@ -338,8 +343,11 @@ PBA_API size_t pba_bwd_workspace_bytes(int B, int S, int Hq, int D);
  * and kmap with the tile shape of pba_bwd_tile (the dK / dV stage walks key
  * tiles).  workspace: device memory of at least pba_bwd_workspace_bytes,
  * 256-byte aligned, contents irrelevant (overwritten).  Every output
- * element is written exactly once (no accumulation into the outputs, no
- * atomics), so the result is deterministic.  softmax_scale > 0. */
+ * element is written exactly once (no accumulation into the outputs); the
+ * two fp32 partial sums of a split key tile are added by whichever of its
+ * two workgroups finishes second (an arrival counter decides), and a + b is
+ * b + a, so the result is deterministic.  Calls that overlap on one
+ * workspace race.  softmax_scale > 0. */
 PBA_API int pba_packed_attn_bwd(const pba_block_map* qmap, const pba_block_map* kmap, const void* q, const void* k,
                                 const void* v, const void* o, const float* lse, const void* dout, void* dq, void* dk,
                                 void* dv, void* workspace, size_t workspace_bytes, int B, int S, int Hq, int Hkv,
