@@ -157,7 +157,7 @@ TRAFFIC_KERNELS = {  # record name -> (kernel name prefix in rocprofv3 output, s
 }
 
 
-def write_traffic(fetch_csv, write_csv, workload):
+def write_traffic(fetch_csv, write_csv, workload, out_dir=None):
     """profiles/traffic_<kernel>.json from two rocprofv3 --pmc runs of
     `bench.py --copy-calibration` (FETCH_SIZE, then WRITE_SIZE; KiB per
     dispatch), each scaled by what the same counter reads for the plain
@@ -199,7 +199,7 @@ def write_traffic(fetch_csv, write_csv, workload):
                "fetch_kib_raw": fk, "write_kib_raw": wk, "fetch_scale": fetch_scale, "write_scale": write_scale,
                "read_bytes_per_launch": fk * fetch_scale * 1024, "write_bytes_per_launch": wk * write_scale * 1024}
         rec["hbm_bytes_per_launch"] = rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"]
-        with open(os.path.join(ROOT, "profiles", f"traffic_{rec_name}.json"), "w") as f:
+        with open(os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"traffic_{rec_name}.json"), "w") as f:
             json.dump(rec, f, indent=1)
         log(f"{rec_name}: read {rec['read_bytes_per_launch'] / 1e6:.1f} MB, write "
             f"{rec['write_bytes_per_launch'] / 1e6:.1f} MB per launch ({n} dispatches); "

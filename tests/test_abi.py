@@ -145,3 +145,52 @@ def test_rope_argument_errors():
     assert lib.pba_packed_rope(ctypes.byref(m), 16, 16, 2, 64, 1.0, 0, None) == -11
     assert lib.pba_packed_rope(ctypes.byref(m), 16, 16, 2, 64, float("inf"), 0, None) == -11
     assert lib.pba_packed_rope(ctypes.byref(m), 24, 16, 2, 64, 1e4, 0, None) == -9
+
+
+def test_backward_workspace_layout():
+    """Two fp32 [B, Hq, S] arrays, then the split area of the dK / dV stage:
+    arrival counters (+1 for the split count) and 2 x 2 fp32 blocks of
+    128 keys x D per (key tile, kv head) pair, at most 256 pairs."""
+    import block_sparse_attention_pack_amd as P
+    A = P.api
+    al = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    for B, S, Hq, D in [(1, 144, 2, 64), (8, 1828, 32, 128), (2, 100, 4, 64), (1, 131072, 32, 128)]:
+        pairs = min(256, B * -(-S // 128) * Hq)
+        want = 2 * al(B * Hq * S * 4) + al((pairs + 1) * 4) + pairs * 2 * 2 * 128 * D * 4
+        assert A.workspace_bytes(B, S, Hq, D) == want, (B, S, Hq, D)
+
+
+def test_traffic_records_from_counter_csv(tmp_path):
+    """bench.py --write-traffic: per-kernel averages of FETCH_SIZE / WRITE_SIZE,
+    scaled by the 2^28-byte calibration copy (small copies ignored)."""
+    import csv
+    import json
+    import bench
+
+    names = {"fwd": "void pba::(anonymous namespace)::fwd_kernel<128, 4, false>(pba::FwdArgs)",
+             "bwd_dq": "void pba::(anonymous namespace)::bwd_dq<128, 4>(pba::BwdArgs)",
+             "bwd_dkdv": "void pba::(anonymous namespace)::bwd_dkdv<128>(pba::BwdArgs)"}
+
+    def write(path, counter, copy_kib, vals):
+        with open(path, "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            w.writerow({"Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": 512, "Counter_Name": counter,
+                        "Counter_Value": 3})
+            for _ in range(3):
+                w.writerow({"Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": 131072, "Counter_Name": counter,
+                            "Counter_Value": copy_kib})
+            for k, (a, b) in vals.items():
+                for v in (a, b):
+                    w.writerow({"Kernel_Name": names[k], "Grid_Size": 1024, "Counter_Name": counter,
+                                "Counter_Value": v})
+
+    write(tmp_path / "f.csv", "FETCH_SIZE", 131072, {"fwd": (100, 300), "bwd_dq": (10, 10), "bwd_dkdv": (1, 3)})
+    write(tmp_path / "w.csv", "WRITE_SIZE", 262144, {"fwd": (50, 50), "bwd_dq": (20, 20), "bwd_dkdv": (2, 2)})
+    bench.write_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "test", out_dir=str(tmp_path))
+    rec = json.load(open(tmp_path / "traffic_fwd.json"))
+    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+    assert rec["read_bytes_per_launch"] == 200 * 2.0 * 1024
+    assert rec["write_bytes_per_launch"] == 50 * 1024
+    assert rec["sources_sha256"] == bench.sources_sha256(rec["sources"])
+    assert json.load(open(tmp_path / "traffic_bwd_dkdv.json"))["read_bytes_per_launch"] == 2 * 2.0 * 1024
