@@ -1,4 +1,4 @@
-// Backward kernels of packed branch-aware attention (no atomics).
+// Backward kernels of packed branch-aware attention (no atomic accumulation).
 //
 // For the loss <dO, O> with P = softmax(scale * Q K^T under the mask):
 //   dV = P^T dO,  dP = dO V^T,  dS = P (dP - Delta),  dQ = scale dS K,
