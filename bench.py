@@ -502,7 +502,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path (packs and kv-head groups "
-              "shard with no exchange; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+              "shard with no exchange). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
