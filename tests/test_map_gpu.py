@@ -136,3 +136,13 @@ def test_work_order_large_map():
     ps = random_packset(rng, B=40, S=1000, max_packs_per_row=4, max_resp=4, max_len=120)
     say("map large order", ps.B, ps.S, len(ps.packs))
     _compare_multi(ps, [(16, 16), (16, 64)])
+
+
+@pytest.mark.parametrize("S", [1024, 1025])
+def test_work_order_at_the_lds_sort_limit(S):
+    """Exactly 2048 tiles per side (sorted by rank in LDS by the last list
+    workgroup) and 2080 (the counting-sort pass): both bit-exact."""
+    rng = np.random.default_rng(91)
+    ps = random_packset(rng, B=32, S=S, max_packs_per_row=3, max_resp=4, max_len=200)
+    say("map order limit", ps.B, ps.S, len(ps.packs))
+    _compare_multi(ps, [(16, 16), (16, 64)])
