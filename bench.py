@@ -224,6 +224,40 @@ def measured_mfma_peak(A, torch):
     return best
 
 
+def unit_rates(A, torch):
+    """Sustained rates of the units the attention kernels share, from the
+    library's probe loops: LDS reads (TB/s and bytes per clock per CU at the
+    nominal 2.4 GHz), fp32 FMA and exp2 issue rates (wave64 instructions per
+    SIMD per nominal clock; the exp2 loop pairs each v_exp_f32 with one
+    multiply)."""
+    def best_ms(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        return best
+
+    clk, cus, simds = 2.4e9, 256, 1024
+    nb, it = 2048, 2000
+    out = torch.empty(nb * 512, dtype=torch.float32, device="cuda")
+    ms = best_ms(lambda: A.lds_probe(out, nb, it))
+    lds = nb * 512 * 256 * it / (ms * 1e-3)
+    rates = {"lds_read_TBps": lds / 1e12, "lds_read_B_per_clk_per_cu": lds / cus / clk}
+    nb, it = 8192, 1000
+    out = torch.empty(nb * 256, dtype=torch.float32, device="cuda")
+    for name, e in (("fma", False), ("exp2_plus_mul", True)):
+        ms = best_ms(lambda: A.valu_probe(out, nb, it, e))
+        rates[f"{name}_wave64_per_simd_clk"] = nb * 4 * 16 * it / (ms * 1e-3) / simds / clk
+    rates["exp2_cycles_est"] = 1 / rates["exp2_plus_mul_wave64_per_simd_clk"] - 1 / rates["fma_wave64_per_simd_clk"]
+    return rates
+
+
 def copy_bandwidth(torch):
     """Device-to-device copy rate (read + write bytes per second), GB/s."""
     src = torch.ones(1 << 27, dtype=torch.bfloat16, device="cuda")
@@ -606,6 +640,8 @@ def main():
     extra["frac_of_measured_peak"] = value / peak_meas
     roofline["frac_of_measured_peak"] = achieved / peak_meas
     log(f"measured MFMA peak {peak_meas:.0f} TFLOP/s: step at {value / peak_meas:.3f}, {dom} at {achieved / peak_meas:.3f}")
+    extra["unit_rates"] = unit_rates(A, torch)
+    log(f"unit rates: {json.dumps({k_: round(v_, 3) for k_, v_ in extra['unit_rates'].items()})}")
     if not args.no_baselines:
         gbps = copy_bandwidth(torch)
         extra["copy_GBps"] = gbps

@@ -26,7 +26,7 @@ PBA_OK = 0
 TILE_SKIP, TILE_PARTIAL, TILE_FULL = 0, 1, 2
 EXPORTED = ("pba_strerror", "pba_fwd_tile", "pba_bwd_tile", "pba_map_bytes", "pba_map_init",
             "pba_pack_block_map", "pba_pack_block_maps", "pba_packed_attn_fwd", "pba_bwd_workspace_bytes", "pba_packed_attn_bwd",
-            "pba_packed_attn_bwd_stages", "pba_mfma_probe", "pba_pack_positions",
+            "pba_packed_attn_bwd_stages", "pba_mfma_probe", "pba_lds_probe", "pba_valu_probe", "pba_pack_positions",
             "pba_packed_token_logp", "pba_group_coefficients", "pba_packed_rope", "pba_packed_attn_bwd_rope",
             "pba_packed_attn_fwd_rope")
 
@@ -92,6 +92,10 @@ _lib.pba_packed_attn_fwd_rope.argtypes = [ctypes.POINTER(PbaBlockMap)] + [ctypes
 _lib.pba_packed_attn_fwd_rope.restype = ctypes.c_int
 _lib.pba_mfma_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
 _lib.pba_mfma_probe.restype = ctypes.c_int
+_lib.pba_lds_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+_lib.pba_lds_probe.restype = ctypes.c_int
+_lib.pba_valu_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+_lib.pba_valu_probe.restype = ctypes.c_int
 BWD_DQ, BWD_DKDV, BWD_ALL = 1, 2, 3
 
 
@@ -365,6 +369,22 @@ def mfma_probe(out: torch.Tensor, n_blocks: int, iters: int, stream=None) -> Non
     if out.dtype != torch.float32 or out.numel() < n_blocks * 256 or not out.is_cuda:
         raise ValueError("out must be a float32 device tensor of n_blocks * 256 elements")
     _check(_lib.pba_mfma_probe(out.data_ptr(), n_blocks, iters, _stream(stream)), "pba_mfma_probe")
+
+
+def lds_probe(out: torch.Tensor, n_blocks: int, iters: int, stream=None) -> None:
+    """Enqueue the library's LDS read-bandwidth loop (a measurement helper);
+    `out` is a float32 device tensor of at least n_blocks * 512 elements."""
+    if out.dtype != torch.float32 or out.numel() < n_blocks * 512 or not out.is_cuda:
+        raise ValueError("out must be a float32 device tensor of n_blocks * 512 elements")
+    _check(_lib.pba_lds_probe(out.data_ptr(), n_blocks, iters, _stream(stream)), "pba_lds_probe")
+
+
+def valu_probe(out: torch.Tensor, n_blocks: int, iters: int, exp2: bool, stream=None) -> None:
+    """Enqueue the library's FMA (exp2=False) or exp2 + multiply (exp2=True)
+    issue-rate loop; `out` is a float32 device tensor of n_blocks * 256."""
+    if out.dtype != torch.float32 or out.numel() < n_blocks * 256 or not out.is_cuda:
+        raise ValueError("out must be a float32 device tensor of n_blocks * 256 elements")
+    _check(_lib.pba_valu_probe(out.data_ptr(), n_blocks, iters, int(bool(exp2)), _stream(stream)), "pba_valu_probe")
 
 
 def pack_positions(m: BlockMap, out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None, stream=None):

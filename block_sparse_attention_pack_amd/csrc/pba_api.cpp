@@ -504,6 +504,8 @@ int pba_packed_attn_bwd(const pba_block_map* qmap, const pba_block_map* kmap, co
 
 namespace pba {
 hipError_t launch_mfma_probe(float* out, int n_blocks, int iters, hipStream_t stream);  // pba_probe.hip
+hipError_t launch_lds_probe(float* out, int n_blocks, int iters, hipStream_t stream);
+hipError_t launch_valu_probe(float* out, int n_blocks, int iters, int exp, hipStream_t stream);
 }
 
 extern "C" {
@@ -513,6 +515,21 @@ int pba_mfma_probe(float* out, int n_blocks, int iters, void* stream) {
   if (n_blocks < 1 || n_blocks > (1 << 20) || iters < 1) return PBA_ERR_SHAPE;
   if (int rc = device_ok()) return rc;
   return pba::launch_mfma_probe(out, n_blocks, iters, (hipStream_t)stream) == hipSuccess ? PBA_OK : PBA_ERR_DEVICE;
+}
+
+int pba_lds_probe(float* out, int n_blocks, int iters, void* stream) {
+  if (!out) return PBA_ERR_NULL;
+  if (n_blocks < 1 || n_blocks > (1 << 20) || iters < 1) return PBA_ERR_SHAPE;
+  if (int rc = device_ok()) return rc;
+  return pba::launch_lds_probe(out, n_blocks, iters, (hipStream_t)stream) == hipSuccess ? PBA_OK : PBA_ERR_DEVICE;
+}
+
+int pba_valu_probe(float* out, int n_blocks, int iters, int exp2, void* stream) {
+  if (!out) return PBA_ERR_NULL;
+  if (n_blocks < 1 || n_blocks > (1 << 20) || iters < 1 || (exp2 != 0 && exp2 != 1)) return PBA_ERR_SHAPE;
+  if (int rc = device_ok()) return rc;
+  return pba::launch_valu_probe(out, n_blocks, iters, exp2, (hipStream_t)stream) == hipSuccess ? PBA_OK
+                                                                                             : PBA_ERR_DEVICE;
 }
 
 }  // extern "C"

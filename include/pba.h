@@ -393,6 +393,22 @@ PBA_API int pba_packed_attn_bwd_rope(const pba_block_map* qmap, const pba_block_
  * PBA_ERR_DEVICE. */
 PBA_API int pba_mfma_probe(float* out, int n_blocks, int iters, void* stream);
 
+/* Measurement helper: n_blocks workgroups of 512 threads, each filling a
+ * 64 KB LDS array and then reading `iters` x 16 times 16 bytes per thread
+ * from it (lane-contiguous, no bank conflicts), i.e.
+ * n_blocks * 512 * 256 * iters bytes of LDS reads; one float per thread to
+ * `out` (device, n_blocks * 512 floats).  Timing it gives the sustained LDS
+ * read bandwidth.  Errors as pba_mfma_probe. */
+PBA_API int pba_lds_probe(float* out, int n_blocks, int iters, void* stream);
+
+/* Measurement helper: n_blocks workgroups of 256 threads, each thread
+ * running `iters` x 16 independent fp32 FMAs (exp2 = 0), or 16 times
+ * v_exp_f32 followed by one multiply (exp2 = 1); one float per thread to
+ * `out` (device, n_blocks * 256 floats).  Timing it gives the vector-ALU
+ * and the transcendental issue rates.  Errors as pba_mfma_probe
+ * (PBA_ERR_SHAPE also for exp2 outside {0, 1}). */
+PBA_API int pba_valu_probe(float* out, int n_blocks, int iters, int exp2, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

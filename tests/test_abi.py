@@ -101,6 +101,11 @@ def test_positions_and_probe_argument_errors():
     assert lib.pba_mfma_probe(None, 1, 1, None) == -1
     assert lib.pba_mfma_probe(16, 0, 1, None) == -2
     assert lib.pba_mfma_probe(16, 1, 0, None) == -2
+    assert lib.pba_lds_probe(None, 1, 1, None) == -1
+    assert lib.pba_lds_probe(16, 0, 1, None) == -2
+    assert lib.pba_valu_probe(None, 1, 1, 0, None) == -1
+    assert lib.pba_valu_probe(16, 1, 0, 1, None) == -2
+    assert lib.pba_valu_probe(16, 1, 1, 2, None) == -2
 
 
 def test_group_coefficients_argument_errors():
