@@ -150,10 +150,12 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   // Workgroup 0 prepares bwd_dkdv's split key tiles: the arrival counters
   // start at zero, and the number of leading work-order positions whose
-  // list is longer than the average load of a workgroup slot (all visited
-  // tiles of the key-major map over the slots of one kv group) is stored
-  // after them.  The work order is longest first, so those positions are a
-  // prefix of it.
+  // list is more than 1.05 times the average load of a workgroup slot (all
+  // visited tiles of the key-major map over the slots of one kv group) is
+  // stored after them: a tile within about one workgroup prologue of the
+  // average gains less from splitting than the second workgroup's prologue
+  // and the exchange cost.  The work order is longest first, so those
+  // positions are a prefix of it.
   if (blockIdx.x == 0) {
     for (int i = tid; i < a.nsplit * a.Hkv; i += 256) a.arrive[i] = 0;
     bool split = false;
@@ -161,7 +163,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
       const MapView& km = a.kmap;
       const int it = min(max(km.k_order[tid], 0), km.B * km.nkt - 1);
       const int n = min(max(km.k2q_cnt[2 * it] + km.k2q_cnt[2 * it + 1], 0), km.nqt);
-      split = (int64_t)n * a.slots > km.totals[0] + km.totals[1];
+      split = 20 * (int64_t)n * a.slots > 21 * (km.totals[0] + km.totals[1]);
     }
     const int nsp = __syncthreads_count(split);
     if (tid == 0) a.arrive[a.nsplit * a.Hkv] = nsp;

@@ -183,10 +183,10 @@ def test_split_key_tiles_deterministic():
     fm = A.pack_block_map(pd, rd, w.packset.B, w.packset.S, *A.fwd_tile(w.Hq, w.Hkv, w.D))
     bm = A.pack_block_map(pd, rd, w.packset.B, w.packset.S, *A.bwd_tile(w.Hq, w.Hkv, w.D))
     o, lse = A.packed_attn_fwd(fm, q, k, v, w.scale)
-    # The host's reading of the split rule: lists longer than visited / slots.
+    # The host's reading of the split rule: lists longer than 1.05 x visited / slots.
     cnt = bm.k2q_cnt().cpu().numpy().reshape(-1, 2).sum(1)
     slots = max(1, torch.cuda.get_device_properties(0).multi_processor_count // w.Hkv)
-    assert (cnt * slots > cnt.sum()).sum() >= 8
+    assert (20 * cnt * slots > 21 * cnt.sum()).sum() >= 8
     ws = torch.empty(A.workspace_bytes(w.packset.B, w.packset.S, w.Hq, w.D) + 256, dtype=torch.uint8, device=dev)
     runs = []
     for fill in (0, 255, 7):
