@@ -4,11 +4,13 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <mutex>
 
 #include "pba_next.h"
+#include "../../include/pba_measure.h"
 
 namespace {
 
@@ -100,6 +102,10 @@ size_t split_pairs(int B, int S, int Hq) {
   const size_t nkt = (size_t)((S + pba::kBwdBN - 1) / pba::kBwdBN);
   return std::min((size_t)pba::kMaxSplitPairs, (size_t)B * nkt * Hq);
 }
+
+// Workgroup slots per kv group for the split rule of bwd_dkdv when set by
+// pba_set_bwd_split_slots (0: the device's compute units / Hkv).
+std::atomic<int> g_split_slots{0};
 
 // Compute units of the current device, cached per device (0 if unknown).
 int cu_count() {
@@ -466,7 +472,8 @@ int bwd_impl(int stages, const pba_block_map* qmap, const pba_block_map* kmap, c
   char* split_base = static_cast<char*>(workspace) + 2 * align_up((size_t)B * Hq * S * 4);
   a.arrive = reinterpret_cast<int32_t*>(split_base);
   a.part = reinterpret_cast<float*>(split_base + align_up((pairs + 1) * 4));
-  a.slots = std::max(1, cu_count() / Hkv);
+  const int fixed_slots = g_split_slots.load(std::memory_order_relaxed);
+  a.slots = fixed_slots > 0 ? fixed_slots : std::max(1, cu_count() / Hkv);
   a.nsplit = (int)std::min({(size_t)B * kmap->nkt, (size_t)a.slots, pairs / (size_t)Hkv});
   hipError_t e = pba::launch_bwd(a, D, stages, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PBA_OK : PBA_ERR_DEVICE;
@@ -490,6 +497,11 @@ int pba_packed_attn_bwd_rope(const pba_block_map* qmap, const pba_block_map* kma
   if (!(rope_base > 1.f) || !std::isfinite(rope_base)) return PBA_ERR_ARG;
   return bwd_impl(PBA_BWD_ALL, qmap, kmap, q_rot, k_rot, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B,
                   S, Hq, Hkv, D, softmax_scale, rope_base, stream);
+}
+
+int pba_set_bwd_split_slots(int slots) {
+  if (slots < 0) return PBA_ERR_SHAPE;
+  return g_split_slots.exchange(slots);
 }
 
 int pba_packed_attn_bwd(const pba_block_map* qmap, const pba_block_map* kmap, const void* q, const void* k,

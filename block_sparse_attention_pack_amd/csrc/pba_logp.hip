@@ -37,6 +37,28 @@ __device__ __forceinline__ LseAcc lse_merge(LseAcc a, LseAcc b) {
 __device__ __forceinline__ float bf16_lo(unsigned u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
 
+// Folds 8 logits (one 16-byte chunk) into the running (max, sum).  While
+// every logit seen so far is -inf the max stays -inf; the exponent
+// reference is then 0 instead, so that the terms are 2^-inf = 0 rather than
+// 2^(-inf - -inf) = NaN.
+__device__ __forceinline__ LseAcc fold8(LseAcc acc, const u32x4& v) {
+  float x[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = bf16_lo(v[k]);
+    x[2 * k + 1] = bf16_hi(v[k]);
+  }
+  float mx = x[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) mx = fmaxf(mx, x[k]);
+  const float nm = fmaxf(acc.m, mx * kLog2e);
+  const float ref = nm == -__builtin_inff() ? 0.f : nm;
+  float s = acc.s * fast_exp2(acc.m - ref);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s += fast_exp2(__builtin_fmaf(x[k], kLog2e, -ref));
+  return {nm, s};
+}
+
 __global__ void __launch_bounds__(kLpThreads) token_logp(LogpArgs a) {
   if (a.status[0] != 0) return;
   const int64_t t = blockIdx.x;
@@ -57,40 +79,9 @@ __global__ void __launch_bounds__(kLpThreads) token_logp(LogpArgs a) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) v[u] = row[c + u * kLpThreads];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      float x[8];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        x[2 * k] = bf16_lo(v[u][k]);
-        x[2 * k + 1] = bf16_hi(v[u][k]);
-      }
-      float mx = x[0];
-#pragma unroll
-      for (int k = 1; k < 8; ++k) mx = fmaxf(mx, x[k]);
-      const float nm = fmaxf(acc.m, mx * kLog2e);
-      float s = acc.s * fast_exp2(acc.m - nm);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) s += fast_exp2(__builtin_fmaf(x[k], kLog2e, -nm));
-      acc = {nm, s};
-    }
+    for (int u = 0; u < kUnroll; ++u) acc = fold8(acc, v[u]);
   }
-  for (; c < nch; c += kLpThreads) {
-    const u32x4 v = row[c];
-    float x[8];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x[2 * k] = bf16_lo(v[k]);
-      x[2 * k + 1] = bf16_hi(v[k]);
-    }
-    float mx = x[0];
-#pragma unroll
-    for (int k = 1; k < 8; ++k) mx = fmaxf(mx, x[k]);
-    const float nm = fmaxf(acc.m, mx * kLog2e);
-    float s = acc.s * fast_exp2(acc.m - nm);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) s += fast_exp2(__builtin_fmaf(x[k], kLog2e, -nm));
-    acc = {nm, s};
-  }
+  for (; c < nch; c += kLpThreads) acc = fold8(acc, row[c]);
   // Workgroup reduction of (max, sum): within each wave, then across waves.
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {

@@ -369,6 +369,23 @@ PBA_API int pba_packed_attn_bwd_stages(int stages, const pba_block_map* qmap, co
                                        size_t workspace_bytes, int B, int S, int Hq, int Hkv, int D,
                                        float softmax_scale, void* stream);
 
+/* Rounding of dK / dV and the compute-unit count.  A key tile whose visit
+ * list is longer than 1.05 times the average load of one workgroup slot
+ * (all visited tiles of kmap over `slots`, the slots per kv group) is
+ * split between two workgroups; its dK / dV are then the sum of two fp32
+ * partial sums, one per half of its list, instead of one running sum.  By
+ * default slots = compute units of the device / Hkv, so which tiles are
+ * split, and with it the last bits of their dK / dV, depends on the device's
+ * CU count: results are bit-identical from run to run on one device (and
+ * across devices with the same count) but may differ in rounding between
+ * devices or partition modes with different counts (both stay within the
+ * same error bound of exact arithmetic).  pba_set_bwd_split_slots(n) fixes
+ * slots = n for every later backward call of this process (n >= 1), or
+ * restores the default (n = 0), and returns the previous setting (0 for
+ * the default); PBA_ERR_SHAPE for n < 0.  Process-wide: set it before
+ * calls are enqueued, not while another thread enqueues one. */
+PBA_API int pba_set_bwd_split_slots(int slots);
+
 /* Backward for rotary inputs, with the rotation of the gradients fused in.
  * q_rot, k_rot are Q and K rotated by pba_packed_rope at the packed
  * positions (with this base); o and lse come from pba_packed_attn_fwd on
@@ -382,32 +399,6 @@ PBA_API int pba_packed_attn_bwd_rope(const pba_block_map* qmap, const pba_block_
                                      const void* dout, void* dq, void* dk, void* dv, void* workspace,
                                      size_t workspace_bytes, int B, int S, int Hq, int Hkv, int D,
                                      float softmax_scale, float rope_base, void* stream);
-
-/* Measurement helper, not an operation of the method: enqueues n_blocks
- * workgroups of 256 threads that each run `iters` iterations of 16 bf16
- * MFMAs (v_mfma_f32_32x32x16_bf16, 32768 FLOP each) per wave, i.e.
- * n_blocks * 4 * iters * 16 * 32768 FLOP, and write one float per thread
- * to `out` (device, caller-allocated, n_blocks * 256 floats).  Timing it
- * gives the sustained MFMA rate of the device.  Returns PBA_OK,
- * PBA_ERR_NULL, PBA_ERR_SHAPE (n_blocks outside 1..2^20 or iters < 1) or
- * PBA_ERR_DEVICE. */
-PBA_API int pba_mfma_probe(float* out, int n_blocks, int iters, void* stream);
-
-/* Measurement helper: n_blocks workgroups of 512 threads, each filling a
- * 64 KB LDS array and then reading `iters` x 16 times 16 bytes per thread
- * from it (lane-contiguous, no bank conflicts), i.e.
- * n_blocks * 512 * 256 * iters bytes of LDS reads; one float per thread to
- * `out` (device, n_blocks * 512 floats).  Timing it gives the sustained LDS
- * read bandwidth.  Errors as pba_mfma_probe. */
-PBA_API int pba_lds_probe(float* out, int n_blocks, int iters, void* stream);
-
-/* Measurement helper: n_blocks workgroups of 256 threads, each thread
- * running `iters` x 16 independent fp32 FMAs (exp2 = 0), or 16 times
- * v_exp_f32 followed by one multiply (exp2 = 1); one float per thread to
- * `out` (device, n_blocks * 256 floats).  Timing it gives the vector-ALU
- * and the transcendental issue rates.  Errors as pba_mfma_probe
- * (PBA_ERR_SHAPE also for exp2 outside {0, 1}). */
-PBA_API int pba_valu_probe(float* out, int n_blocks, int iters, int exp2, void* stream);
 
 #ifdef __cplusplus
 }

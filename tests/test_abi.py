@@ -18,9 +18,19 @@ def lib():
     return ctypes.CDLL(LIB)
 
 
-def _declared():
-    src = open(os.path.join(ROOT, "include", "pba.h")).read()
-    return sorted(set(re.findall(r"PBA_API\s+[\w\s\*]+?\b(pba_\w+)\s*\(", src)))
+def _declared(headers=None):
+    """Every pba_* function declared in include/*.h (or the named headers)."""
+    inc = os.path.join(ROOT, "include")
+    names = set()
+    for h in headers or sorted(f for f in os.listdir(inc) if f.endswith(".h")):
+        src = open(os.path.join(inc, h)).read()
+        names |= set(re.findall(r"PBA_API\s+[\w\s\*]+?\b(pba_\w+)\s*\(", src))
+    return sorted(names)
+
+
+def test_probes_live_outside_the_method_header():
+    assert not {"pba_mfma_probe", "pba_lds_probe", "pba_valu_probe"} & set(_declared(["pba.h"]))
+    assert {"pba_mfma_probe", "pba_lds_probe", "pba_valu_probe"} <= set(_declared(["pba_measure.h"]))
 
 
 def test_header_declares_the_three_calls():

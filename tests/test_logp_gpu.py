@@ -123,6 +123,36 @@ def test_full_vocab_sampled():
     del logits
 
 
+def test_leading_masked_logits():
+    """Rows whose leading logits are -inf (masked vocabulary entries): every
+    lane's first chunks see nothing but -inf, which must not turn the running
+    log-sum-exp into NaN.  The first 4096 of V = 8192 logits of every row
+    are -inf; tokens in the masked part get -inf, the others the oracle's
+    value."""
+    ps = make_packset(1)
+    V = 8192
+    logits, tokens = _inputs(ps, V, 4)
+    logits[:, :, :4096] = float("-inf")
+    tokens[0, ::2] = 0  # masked token id
+    P, R = descriptor_arrays(ps)
+    A = api()
+    pd, rd = A.descriptors_to_device(P, R)
+    m = A.pack_block_map(pd, rd, ps.B, ps.S, 64, 64)
+    pos, src, mask = A.pack_positions(m)
+    tok, _ = A.packed_token_logp(m, src, mask, logits.cuda().contiguous(), tokens.cuda(), pd, rd)
+    torch.cuda.synchronize()
+    got = tok.cpu().double().numpy()
+    _, osrc, omask, _ = oracle.positions(P, R, ps.B, ps.S)
+    lf = logits.float()
+    want = oracle.token_logp(lambda b, r: lf[b, r].numpy(), tokens.numpy(), osrc, omask)
+    say("logp leading -inf logits", int(np.isnan(got).sum()))
+    assert not np.isnan(got).any()
+    inf = np.isneginf(want)
+    assert inf.any() and (~inf & (omask == 1)).any()
+    assert np.array_equal(np.isneginf(got), inf)
+    assert float(np.abs(got[~inf] - want[~inf]).max()) <= TOK_ABS
+
+
 def test_bad_token_and_invalid_map():
     A = api()
     ps = make_packset(1)

@@ -30,6 +30,20 @@ def test_two_level_closed_form(a, b, V):
     assert abs((x[0] - lse) - (b - norm)) < 1e-10
 
 
+@pytest.mark.parametrize("k,V", [(8, 16), (4096, 8192), (1, 2)])
+def test_masked_logits_closed_form(k, V):
+    """Logits masked to -inf drop out of the normaliser: with k of them and
+    V - k equal finite logits c, a finite token has log-prob -ln(V - k) and
+    a masked token -inf."""
+    x = np.full(V, 1.5)
+    x[:k] = -np.inf
+    assert abs(oracle.row_logsumexp(x) - (1.5 + math.log(V - k))) < 1e-12
+    tok = np.array([[V - 1, 0]], dtype=np.int32)
+    got = oracle.token_logp(lambda b, r: x, tok, np.zeros((1, 2), np.int32), np.ones((1, 2), np.uint8))
+    assert abs(got[0, 0] + math.log(V - k)) < 1e-12
+    assert got[0, 1] == -np.inf
+
+
 def test_shift_invariance_and_normalisation():
     rng = np.random.default_rng(3)
     x = rng.normal(0, 3, size=5000)

@@ -49,12 +49,12 @@ def test_p5_positions_and_target_boundaries(golden_dir):
 
 
 def test_p1_branch_start_reads_the_last_prompt_row():
-    """The tiny pack (prompt 64, chosen 32, rejected 48): both responses'
-    first tokens are predicted from the final prompt row, and both start at
-    position 64 ("DPO Preference Packing: Dense Masks and Sparse Execution",
-    section "Layout requirements").  A one-position shift over the packed
-    sequence would read the rejected branch's first token from the end of
-    the chosen branch (row 95)."""
+    """Tiny pack (prompt 64, chosen 32, rejected 48), rows 0-143: the
+    responses begin at rows 64 and 96, both at position id 64, and the
+    source row of each of those two tokens is 63.  Asserted against the
+    plain shift src = s - 1, which gives 95 for row 96 ("DPO Preference
+    Packing: Dense Masks and Sparse Execution", section "Layout
+    requirements")."""
     ps = make_packset(1, 0)
     P, R = descriptor_arrays(ps)
     pos, src, mask, st = oracle.positions(P, R, ps.B, ps.S)
