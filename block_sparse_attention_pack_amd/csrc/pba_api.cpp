@@ -96,6 +96,8 @@ int check_heads(int B, int S, int Hq, int Hkv, int D) {
   return PBA_OK;
 }
 
+size_t bwd_scratch_bytes(int B, int S, int Hq, int D, size_t pairs);
+
 // Split key tiles of bwd_dkdv: at most this many (position, kv group)
 // pairs have a partial-sum area in the workspace.
 size_t split_pairs(int B, int S, int Hq) {
@@ -417,17 +419,22 @@ int pba_packed_attn_fwd_rope(const pba_block_map* map, const void* q, const void
 
 size_t pba_bwd_workspace_bytes(int B, int S, int Hq, int D) {
   if (B < 1 || B > kMaxB || S < 1 || S > kMaxS || Hq < 1 || Hq > kMaxHeads || (D != 64 && D != 128)) return 0;
-  const size_t pairs = split_pairs(B, S, Hq);
-  return 2 * align_up((size_t)B * Hq * S * 4) + align_up((pairs + 1) * 4) + pairs * 2 * 2 * pba::kBwdBN * D * 4;
+  return bwd_scratch_bytes(B, S, Hq, D, split_pairs(B, S, Hq));
 }
 
 }  // extern "C"
 
 namespace {
-int bwd_impl(int stages, const pba_block_map* qmap, const pba_block_map* kmap, const void* q, const void* k,
-             const void* v, const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
-             void* workspace, size_t workspace_bytes, int B, int S, int Hq, int Hkv, int D, float softmax_scale,
-             float rope_base, void* stream) {
+// Bytes of the backward's scratch with `pairs` split pairs: Delta and LSE2
+// (fp32 [B, Hq, S] each), pairs + 1 arrival counters, the partial sums.
+size_t bwd_scratch_bytes(int B, int S, int Hq, int D, size_t pairs) {
+  return 2 * align_up((size_t)B * Hq * S * 4) + align_up((pairs + 1) * 4) + pairs * 2 * 2 * pba::kBwdBN * D * 4;
+}
+
+// Host checks shared by every backward entry point.
+int bwd_check(int stages, const pba_block_map* qmap, const pba_block_map* kmap, const void* q, const void* k,
+              const void* v, const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+              int S, int Hq, int Hkv, int D, float softmax_scale) {
   if (stages < 1 || stages > PBA_BWD_ALL) return PBA_ERR_SHAPE;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return PBA_ERR_NULL;
   if (int rc = check_heads(B, S, Hq, Hkv, D)) return rc;
@@ -441,10 +448,15 @@ int bwd_impl(int stages, const pba_block_map* qmap, const pba_block_map* kmap, c
   if (int rc = check_map(qmap, B, S, bm, bn)) return rc;
   pba_bwd_tile(Hq, Hkv, D, &bm, &bn);
   if (int rc = check_map(kmap, B, S, bm, bn)) return rc;
-  const size_t need = pba_bwd_workspace_bytes(B, S, Hq, D);
-  if (!workspace || workspace_bytes < need) return PBA_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return PBA_ERR_ALIGN;
-  if (int rc = device_ok()) return rc;
+  return PBA_OK;
+}
+
+// Enqueues the backward's kernels with their scratch at `ws` (256-byte
+// aligned, bwd_scratch_bytes(..., pairs) bytes) after bwd_check passed.
+int bwd_launch(int stages, const pba_block_map* qmap, const pba_block_map* kmap, const void* q, const void* k,
+               const void* v, const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+               void* ws, size_t pairs, int B, int S, int Hq, int Hkv, int D, float softmax_scale, float rope_base,
+               void* stream) {
   pba::BwdArgs a;
   a.qmap = view_of(qmap);
   a.kmap = view_of(kmap);
@@ -457,8 +469,8 @@ int bwd_impl(int stages, const pba_block_map* qmap, const pba_block_map* kmap, c
   a.dq = static_cast<pba::bf16*>(dq);
   a.dk = static_cast<pba::bf16*>(dk);
   a.dv = static_cast<pba::bf16*>(dv);
-  a.delta = static_cast<float*>(workspace);
-  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up((size_t)B * Hq * S * 4));
+  a.delta = static_cast<float*>(ws);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)B * Hq * S * 4));
   a.B = B;
   a.S = S;
   a.Hq = Hq;
@@ -468,8 +480,7 @@ int bwd_impl(int stages, const pba_block_map* qmap, const pba_block_map* kmap, c
   a.scale_log2 = softmax_scale * pba::kLog2eHost;
   a.rope_log2_base = rope_base > 0.f ? std::log2(rope_base) : 0.f;
   // Split area: arrival counters, then the partial sums.
-  const size_t pairs = split_pairs(B, S, Hq);
-  char* split_base = static_cast<char*>(workspace) + 2 * align_up((size_t)B * Hq * S * 4);
+  char* split_base = static_cast<char*>(ws) + 2 * align_up((size_t)B * Hq * S * 4);
   a.arrive = reinterpret_cast<int32_t*>(split_base);
   a.part = reinterpret_cast<float*>(split_base + align_up((pairs + 1) * 4));
   const int fixed_slots = g_split_slots.load(std::memory_order_relaxed);
@@ -477,6 +488,20 @@ int bwd_impl(int stages, const pba_block_map* qmap, const pba_block_map* kmap, c
   a.nsplit = (int)std::min({(size_t)B * kmap->nkt, (size_t)a.slots, pairs / (size_t)Hkv});
   hipError_t e = pba::launch_bwd(a, D, stages, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PBA_OK : PBA_ERR_DEVICE;
+}
+
+int bwd_impl(int stages, const pba_block_map* qmap, const pba_block_map* kmap, const void* q, const void* k,
+             const void* v, const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes, int B, int S, int Hq, int Hkv, int D, float softmax_scale,
+             float rope_base, void* stream) {
+  if (int rc = bwd_check(stages, qmap, kmap, q, k, v, o, lse, dout, dq, dk, dv, B, S, Hq, Hkv, D, softmax_scale))
+    return rc;
+  const size_t pairs = split_pairs(B, S, Hq);
+  if (!workspace || workspace_bytes < bwd_scratch_bytes(B, S, Hq, D, pairs)) return PBA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return PBA_ERR_ALIGN;
+  if (int rc = device_ok()) return rc;
+  return bwd_launch(stages, qmap, kmap, q, k, v, o, lse, dout, dq, dk, dv, workspace, pairs, B, S, Hq, Hkv, D,
+                    softmax_scale, rope_base, stream);
 }
 }  // namespace
 

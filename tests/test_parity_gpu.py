@@ -53,7 +53,20 @@ def test_tiny_config():
     _check_full(w, run_fwd_bwd(w), "tiny")
 
 
-@pytest.mark.parametrize("heads", [(4, 2, 64), (8, 1, 128), (4, 4, 128), (2, 2, 64), (8, 2, 128), (32, 8, 128)])
+# (Hq, Hkv, D) covering every compiled forward / dQ variant: q heads per
+# workgroup WGH = 4 (G % 4 == 0), 2 (G % 4 == 2) and 1 (odd G), each at
+# D = 64 and D = 128, and the dK / dV kernel at both D.
+HEAD_SHAPES = [
+    (8, 2, 128), (32, 8, 128), (8, 1, 128),  # WGH 4, D 128
+    (8, 2, 64), (8, 1, 64),                  # WGH 4, D 64
+    (4, 2, 128), (12, 2, 128),               # WGH 2, D 128 (G = 2, 6)
+    (4, 2, 64),                              # WGH 2, D 64
+    (4, 4, 128), (6, 2, 128),                # WGH 1, D 128 (G = 1, 3)
+    (2, 2, 64), (3, 1, 64),                  # WGH 1, D 64
+]
+
+
+@pytest.mark.parametrize("heads", HEAD_SHAPES)
 @pytest.mark.parametrize("seed", [0, 1])
 def test_random_ragged_packs(heads, seed):
     rng = np.random.default_rng(2000 + seed)
@@ -66,11 +79,12 @@ def test_random_ragged_packs(heads, seed):
     _check_full(w, run_fwd_bwd(w), f"random {heads} {seed}")
 
 
-def test_unscaled_multi_tile():
+@pytest.mark.parametrize("heads", [(8, 2, 128), (4, 2, 128), (8, 1, 64), (8, 2, 64), (2, 2, 64), (6, 2, 128)])
+def test_unscaled_multi_tile(heads):
     ps = PackSet(2, 600, [Pack(0, 0, 200, (150, 170)), Pack(0, 520, 30, (40,)), Pack(1, 7, 64, (128, 64, 1, 200))])
-    w = make_workload(None, 3, packset=ps, heads=(8, 2, 128))
-    say("parity unscaled multi-tile")
-    _check_full(w, run_fwd_bwd(w), "multi")
+    w = make_workload(None, 3, packset=ps, heads=heads)
+    say("parity unscaled multi-tile", heads)
+    _check_full(w, run_fwd_bwd(w), f"multi {heads}")
 
 
 def test_pad_inertness():
@@ -138,7 +152,7 @@ def test_full_size_sampled(cfg, unscaled, seed):
     # forward: sampled rows of sampled heads, every batch row
     for b in range(B):
         mb = oracle.attention_mask(pk, br, row=b)
-        rows = _sample_rows(rng, pk[b], 48)
+        rows = np.union1d(_sample_rows(rng, pk[b], 48), _boundary_rows(w.packset, b))
         for h in rng.choice(w.Hq, size=3, replace=False):
             Os, Ls = oracle.attn_fwd_rows(w.q, w.k, w.v, mb, b, int(h), rows, w.scale)
             o = got["o"][b, rows, int(h)].double()
@@ -149,20 +163,96 @@ def test_full_size_sampled(cfg, unscaled, seed):
         if pad.any():
             assert (got["o"][b, torch.from_numpy(pad)] == 0).all()
             assert torch.isneginf(got["lse"][b][:, torch.from_numpy(pad)]).all()
-    # backward: one (row, kv head) pair, sampled query rows and keys
-    b = int(rng.integers(0, B))
-    g = int(rng.integers(0, w.Hkv))
-    mb = oracle.attention_mask(pk, br, row=b)
-    qrows = _sample_rows(rng, pk[b], 64)
-    krows = _sample_rows(rng, pk[b], 64)
-    dqs, dks, dvs = oracle.attn_bwd_sampled(w.q, w.k, w.v, w.do, mb, b, g, qrows, krows, w.scale)
+    # backward: whole (row, kv group) units against the oracle
+    _check_units(w, got, pk, br, _units(w, rng, n=4 if not unscaled else 2))
+
+
+def _boundary_rows(ps, b):
+    """First and last row of every prompt and response in batch row b."""
+    rows = []
+    for pk in ps.packs:
+        if pk.row != b:
+            continue
+        at = pk.start
+        for n in (pk.prompt_len, *pk.resp_lens):
+            if n > 0:
+                rows += [at, at + n - 1]
+            at += n
+    return np.unique(np.asarray(rows, dtype=np.int64))
+
+
+def _prompt_key_tile(ps, b, tile=128):
+    """All keys of one key tile that lies inside a shared prompt of row b
+    (the longest prompt's first whole tile, or its first tile if shorter)."""
+    packs = [pk for pk in ps.packs if pk.row == b and pk.prompt_len > 0 and len(pk.resp_lens) > 1]
+    if not packs:
+        return np.zeros(0, dtype=np.int64)
+    pk = max(packs, key=lambda x: x.prompt_len)
+    t0 = -(-pk.start // tile) * tile
+    if t0 + tile > pk.start + pk.prompt_len:
+        t0 = pk.start // tile * tile
+    lo, hi = max(t0, pk.start), min(t0 + tile, pk.start + pk.prompt_len)
+    return np.arange(lo, hi, dtype=np.int64)
+
+
+def _units(w, rng, n):
+    """n (batch row, kv group) units: distinct rows first, groups spread."""
+    B, Hkv = w.packset.B, w.Hkv
+    rows = list(range(B)) * (-(-n // B))
+    groups = rng.permutation(np.arange(n) % Hkv)
+    return [(rows[i], int(groups[i])) for i in range(n)]
+
+
+def _check_units(w, got, pk, br, units):
+    """dQ on every response's first and last rows plus sampled rows, dK / dV
+    on all keys of a shared-prompt key tile plus sampled keys, for each
+    (batch row, kv group) unit; rel-L2 per unit and tensor."""
+    rng = np.random.default_rng(11)
     G = w.Hq // w.Hkv
-    dq = torch.stack([got["dq"][b, qrows, h] for h in range(g * G, (g + 1) * G)]).double()
-    for name, x, ref in (("dq", dq, dqs), ("dk", got["dk"][b, krows, g].double(), dks),
-                         ("dv", got["dv"][b, krows, g].double(), dvs)):
-        e = rel_l2(x, ref)
-        say(" ", name, "rel-L2", e)
-        assert e <= G_REL, (name, e)
+    for b, g in units:
+        mb = oracle.attention_mask(pk, br, row=b)
+        qrows = np.union1d(_boundary_rows(w.packset, b), _sample_rows(rng, pk[b], 64))
+        krows = np.union1d(_prompt_key_tile(w.packset, b), _sample_rows(rng, pk[b], 64))
+        dqs, dks, dvs = oracle.attn_bwd_sampled(w.q, w.k, w.v, w.do, mb, b, g, qrows, krows, w.scale)
+        dq = torch.stack([got["dq"][b, qrows, h] for h in range(g * G, (g + 1) * G)]).double()
+        errs = {}
+        for name, x, ref in (("dq", dq, dqs), ("dk", got["dk"][b, krows, g].double(), dks),
+                             ("dv", got["dv"][b, krows, g].double(), dvs)):
+            errs[name] = rel_l2(x, ref)
+        say("  unit", (b, g), len(qrows), "q rows", len(krows), "keys", {k: f"{v:.4f}" for k, v in errs.items()})
+        for name, e in errs.items():
+            assert e <= G_REL, (b, g, name, e)
+
+
+def test_qwen3_packs_every_unit():
+    """Qwen3-8B-shaped packs (8 x 1828, 32/8 heads, D 128): every output
+    element of every (batch row, kv group) unit against the oracle's full
+    forward and backward, with the per-unit rel-L2 of each gradient."""
+    w = make_workload(2, 0)
+    say("parity every unit", w.packset.B, w.packset.S)
+    got = run_fwd_bwd(w)
+    m, pk = _mask(w.packset)
+    O, L = oracle.attn_fwd(w.q, w.k, w.v, m, w.scale)
+    dq, dk, dv = oracle.attn_bwd(w.q, w.k, w.v, w.do, m, w.scale)
+    valid = torch.from_numpy(pk >= 0)
+    o = got["o"].double()
+    assert float((o - O).abs()[valid].max()) <= O_ABS
+    assert rel_l2(o[valid], O[valid]) <= O_REL
+    vl = valid[:, None, :].expand_as(L)
+    assert float((got["lse"].double() - L)[vl].abs().max()) <= LSE_ABS
+    G = w.Hq // w.Hkv
+    worst = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    for b in range(w.packset.B):
+        vb = valid[b]
+        for g in range(w.Hkv):
+            hs = slice(g * G, (g + 1) * G)
+            for name, x, ref in (("dq", got["dq"][b, :, hs], dq[b, :, hs]), ("dk", got["dk"][b, :, g], dk[b, :, g]),
+                                 ("dv", got["dv"][b, :, g], dv[b, :, g])):
+                e = rel_l2(x[vb], ref[vb])
+                worst[name] = max(worst[name], e)
+                assert e <= G_REL, (b, g, name, e)
+                assert (x[~vb] == 0).all(), (b, g, name)
+    say("  worst per-unit rel-L2", worst)
 
 
 def test_split_key_tiles_deterministic():
@@ -209,3 +299,63 @@ def test_split_key_tiles_deterministic():
         e = rel_l2(x, ref)
         say(" ", name, "rel-L2 on prompt keys", e)
         assert e <= G_REL, (name, e)
+
+
+def _split_positions(bm, slots, Hq, Hkv):
+    """The host's reading of the split rule: how many leading work-order
+    positions of the key-major map have a list longer than 1.05 times the
+    visited tiles over `slots`."""
+    cnt = bm.k2q_cnt().cpu().numpy().reshape(-1, 2).sum(1)
+    order = bm.k_order().cpu().numpy()
+    pairs = min(256, bm.B * bm.nkt * Hq)
+    nsplit = min(bm.B * bm.nkt, slots, pairs // Hkv)
+    return int((20 * cnt[order[:nsplit]] * slots > 21 * cnt.sum()).sum())
+
+
+def test_split_slots_override():
+    """The slot count of the dK / dV split rule decides which key tiles are
+    split, and so the rounding of their dK / dV.  Fixed to two different
+    values on the same device (group packs, where the prompt's key tiles
+    split), each setting is bit-stable over repeated runs with the workspace
+    refilled in between and passes the oracle's bar on the shared-prompt
+    keys; the two settings split different numbers of tiles."""
+    A = api()
+    w = make_workload(5)
+    dev = "cuda"
+    q, k, v, do = (x.to(dev).contiguous() for x in (w.q, w.k, w.v, w.do))
+    P, R = descriptor_arrays(w.packset)
+    pd, rd = A.descriptors_to_device(P, R)
+    fm = A.pack_block_map(pd, rd, w.packset.B, w.packset.S, *A.fwd_tile(w.Hq, w.Hkv, w.D))
+    bm = A.pack_block_map(pd, rd, w.packset.B, w.packset.S, *A.bwd_tile(w.Hq, w.Hkv, w.D))
+    o, lse = A.packed_attn_fwd(fm, q, k, v, w.scale)
+    ws = torch.empty(A.workspace_bytes(w.packset.B, w.packset.S, w.Hq, w.D) + 256, dtype=torch.uint8, device=dev)
+    pk, br, _ = oracle.token_ids(P, R, w.packset.B, w.packset.S)
+    mb = oracle.attention_mask(pk, br, row=1)
+    p = w.packset.packs[1].prompt_len
+    krows = np.arange(w.packset.packs[1].start, w.packset.packs[1].start + p, 5)
+    qrows = np.arange(0, w.packset.S, 499)
+    _, dks, dvs = oracle.attn_bwd_sampled(w.q, w.k, w.v, w.do, mb, 1, 3, qrows, krows, w.scale)
+    nsp = {}
+    results = {}
+    prev = A.set_bwd_split_slots(0)
+    try:
+        for slots in (6, 64):
+            A.set_bwd_split_slots(slots)
+            nsp[slots] = _split_positions(bm, slots, w.Hq, w.Hkv)
+            runs = []
+            for fill in (0, 255):
+                ws.fill_(fill)
+                runs.append([x.clone() for x in A.packed_attn_bwd(fm, bm, q, k, v, o, lse, do, w.scale, workspace=ws)])
+                torch.cuda.synchronize()
+            for x, y in zip(runs[0], runs[1]):
+                assert torch.equal(x, y), slots
+            results[slots] = runs[0]
+            _, dk, dv = runs[0]
+            e = (rel_l2(dk[1, krows, 3].cpu(), dks), rel_l2(dv[1, krows, 3].cpu(), dvs))
+            say("  slots", slots, "split positions", nsp[slots], "prompt-key rel-L2", e)
+            assert max(e) <= G_REL, (slots, e)
+    finally:
+        A.set_bwd_split_slots(prev)
+    assert nsp[6] != nsp[64], nsp
+    # dQ never depends on the split; dK / dV of unsplit tiles neither
+    assert torch.equal(results[6][0], results[64][0])

@@ -213,3 +213,37 @@ def test_fused_rope_backward_qwen3_packs_sampled():
     Os, _ = oracle.attn_fwd_rows(qr, kr, w.v, mb, b, h, qrows, w.scale)
     assert _rel(got["o"][b, qrows, h], Os) <= 1e-2
     assert _same_rotation(got["q"].double(), got["qr"].double(), got["qr_u"].double())
+
+
+@pytest.mark.parametrize("heads", [(4, 2, 128), (12, 2, 128), (8, 1, 64), (8, 2, 64), (8, 2, 128), (2, 2, 128),
+                                   (3, 1, 64)])
+def test_fused_rope_variants_vs_oracle(heads):
+    """The fused-rotation forward and backward of every compiled variant (q
+    heads per workgroup 4, 2 and 1 at D = 64 and 128) against the oracle on
+    random ragged packs: O on rotated inputs, dQ and dK rotated back to the
+    unrotated Q and K, dV; whole tensors, every valid element."""
+    from workloads.generate import make_workload
+    rng = np.random.default_rng(4200 + 7 * heads[0] + heads[2])
+    ps = random_packset(rng, B=2, S=int(rng.integers(150, 400)), max_packs_per_row=3, max_resp=3, max_len=110)
+    if not ps.packs:
+        ps = make_packset(1)
+    w = make_workload(None, 6, packset=ps, heads=heads, unscaled=True)
+    base = 1e4
+    say("fused rope variant", heads, ps.B, ps.S, len(ps.packs))
+    got = _rope_case(w, base)
+    pk, br, _ = oracle.token_ids(got["P"], got["R"], ps.B, ps.S)
+    mask = oracle.attention_mask(pk, br)
+    qr, kr = R.packed_rope(w.q, got["pos"], base), R.packed_rope(w.k, got["pos"], base)
+    O, L = oracle.attn_fwd(qr, kr, w.v, mask, w.scale)
+    dqr, dkr, dv = oracle.attn_bwd(qr, kr, w.v, w.do, mask, w.scale)
+    dq, dk = R.packed_rope(dqr, got["pos"], base, inverse=True), R.packed_rope(dkr, got["pos"], base, inverse=True)
+    valid = torch.from_numpy(pk >= 0)
+    o = got["o"].double()
+    assert float((o - O).abs()[valid].max()) <= 1e-2
+    errs = {"o": _rel(got["o"][valid], O[valid])}
+    for name, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
+        errs[name] = _rel(got[name][valid], ref[valid])
+        assert (got[name][~valid] == 0).all(), name
+    say("  rel-L2", errs)
+    assert max(errs.values()) <= 1e-2, errs
+    assert _same_rotation(got["q"].double(), got["qr"].double(), got["qr_u"].double())
