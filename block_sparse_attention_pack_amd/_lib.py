@@ -28,7 +28,7 @@ EXPORTED = ("pba_strerror", "pba_fwd_tile", "pba_bwd_tile", "pba_map_bytes", "pb
             "pba_pack_block_map", "pba_pack_block_maps", "pba_packed_attn_fwd", "pba_bwd_workspace_bytes", "pba_packed_attn_bwd",
             "pba_packed_attn_bwd_stages", "pba_mfma_probe", "pba_lds_probe", "pba_valu_probe", "pba_pack_positions",
             "pba_packed_token_logp", "pba_group_coefficients", "pba_packed_rope", "pba_packed_attn_bwd_rope",
-            "pba_packed_attn_fwd_rope", "pba_set_bwd_split_slots")
+            "pba_packed_attn_fwd_rope", "pba_set_bwd_split_slots", "pba_packed_attn_bwd_noalloc")
 
 
 class PbaBlockMap(ctypes.Structure):
@@ -96,6 +96,10 @@ _lib.pba_lds_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctyp
 _lib.pba_lds_probe.restype = ctypes.c_int
 _lib.pba_valu_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
 _lib.pba_valu_probe.restype = ctypes.c_int
+_lib.pba_packed_attn_bwd_noalloc.argtypes = [ctypes.POINTER(PbaBlockMap)] * 2 + [ctypes.c_void_p] * 9 + \
+    [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_void_p]
+_lib.pba_packed_attn_bwd_noalloc.restype = ctypes.c_int
+NOALLOC_SCRATCH_BYTES = 96 << 20
 _lib.pba_set_bwd_split_slots.argtypes = [ctypes.c_int]
 _lib.pba_set_bwd_split_slots.restype = ctypes.c_int
 BWD_DQ, BWD_DKDV, BWD_ALL = 1, 2, 3
@@ -384,6 +388,34 @@ def packed_attn_bwd(qmap: BlockMap, kmap: BlockMap, q, k, v, o, lse, dout, softm
                                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws, ws_bytes, B, S, Hq, Hkv,
                                            D, scale, _stream(stream)),
            "pba_packed_attn_bwd_stages")
+    return dq, dk, dv
+
+
+def packed_attn_bwd_noalloc(qmap: BlockMap, kmap: BlockMap, q, k, v, o, lse, dout,
+                            softmax_scale: Optional[float] = None,
+                            out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None, stream=None):
+    """packed_attn_bwd through pba_packed_attn_bwd_noalloc: the library's own
+    device scratch instead of a workspace (the C call allocates nothing; pass
+    `out` to keep this wrapper from allocating the outputs)."""
+    B, S, Hq, Hkv, D = _qkv(q, k, v)
+    _map(qmap, "qmap", B, S, q.device)
+    _map(kmap, "kmap", B, S, q.device)
+    _bf16(o, "o", q.shape, q.device)
+    _bf16(dout, "dout", q.shape, q.device)
+    _tensor(lse, "lse", (B, Hq, S), torch.float32, q.device, align=4)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+        _bf16(dq, "dq", q.shape, q.device)
+        _bf16(dk, "dk", k.shape, q.device)
+        _bf16(dv, "dv", k.shape, q.device)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    _check(_lib.pba_packed_attn_bwd_noalloc(ctypes.byref(qmap.struct), ctypes.byref(kmap.struct), q.data_ptr(),
+                                            k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, S, Hq, Hkv, D, scale,
+                                            _stream(stream)),
+           "pba_packed_attn_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -163,6 +163,7 @@ const char* pba_strerror(int code) {
     case PBA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
     case PBA_ERR_SCALE: return "softmax scale must be positive and finite";
     case PBA_ERR_ARG: return "objective, beta, alpha or rotary base out of range";
+    case PBA_ERR_SCRATCH: return "problem too large for the no-allocation backward's scratch (8*B*Hq*S bytes of row statistics must fit)";
     case PBA_DESC_ROW: return "descriptor: row outside [0, B)";
     case PBA_DESC_NEGATIVE: return "descriptor: negative start, length or response count";
     case PBA_DESC_RESP_RANGE: return "descriptor: response range outside resp_len";
@@ -505,6 +506,39 @@ int bwd_impl(int stages, const pba_block_map* qmap, const pba_block_map* kmap, c
 }
 }  // namespace
 
+namespace {
+// Scratch of pba_packed_attn_bwd_noalloc: file-scope device memory, one copy
+// per device, held until the process ends.  On the host, `scratch` names
+// only a stand-in, not device memory: host code uses the device address
+// that hipGetSymbolAddress returns, taken once per device and kept.
+__device__ __align__(256) unsigned char scratch[PBA_NOALLOC_SCRATCH_BYTES];
+
+// Device address of this device's `scratch` (nullptr if it cannot be had).
+void* scratch_address() {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+// Split pairs that fit the scratch next to Delta and LSE2 (at most the
+// workspace's own count, so results match pba_packed_attn_bwd whenever they
+// all fit); -1 when Delta, LSE2 and one counter alone do not fit.
+long long noalloc_pairs(int B, int S, int Hq, int D) {
+  size_t pairs = split_pairs(B, S, Hq);
+  if (bwd_scratch_bytes(B, S, Hq, D, 0) > PBA_NOALLOC_SCRATCH_BYTES) return -1;
+  while (pairs > 0 && bwd_scratch_bytes(B, S, Hq, D, pairs) > PBA_NOALLOC_SCRATCH_BYTES) --pairs;
+  return (long long)pairs;
+}
+}  // namespace
+
 extern "C" {
 
 int pba_packed_attn_bwd_stages(int stages, const pba_block_map* qmap, const pba_block_map* kmap, const void* q,
@@ -522,6 +556,22 @@ int pba_packed_attn_bwd_rope(const pba_block_map* qmap, const pba_block_map* kma
   if (!(rope_base > 1.f) || !std::isfinite(rope_base)) return PBA_ERR_ARG;
   return bwd_impl(PBA_BWD_ALL, qmap, kmap, q_rot, k_rot, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B,
                   S, Hq, Hkv, D, softmax_scale, rope_base, stream);
+}
+
+int pba_packed_attn_bwd_noalloc(const pba_block_map* qmap, const pba_block_map* kmap, const void* q,
+                                const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                                void* dq, void* dk, void* dv, int B, int S, int Hq, int Hkv, int D,
+                                float softmax_scale, void* stream) {
+  if (int rc = bwd_check(PBA_BWD_ALL, qmap, kmap, q, k, v, o, lse, dout, dq, dk, dv, B, S, Hq, Hkv, D,
+                         softmax_scale))
+    return rc;
+  const long long pairs = noalloc_pairs(B, S, Hq, D);
+  if (pairs < 0) return PBA_ERR_SCRATCH;
+  if (int rc = device_ok()) return rc;
+  void* ws = scratch_address();
+  if (!ws) return PBA_ERR_DEVICE;
+  return bwd_launch(PBA_BWD_ALL, qmap, kmap, q, k, v, o, lse, dout, dq, dk, dv, ws, (size_t)pairs, B, S, Hq, Hkv, D,
+                    softmax_scale, 0.f, stream);
 }
 
 int pba_set_bwd_split_slots(int slots) {

@@ -76,6 +76,7 @@ extern "C" {
 #define PBA_ERR_ALIGN      -9  /* a tensor pointer is not 16-byte aligned          */
 #define PBA_ERR_SCALE     -10  /* softmax_scale not positive and finite            */
 #define PBA_ERR_ARG       -11  /* objective, beta, alpha or rotary base out of range */
+#define PBA_ERR_SCRATCH   -12  /* problem larger than the no-allocation backward's scratch */
 
 /* ---- device status codes (map->status[0]; status[1] = first bad pack) -- */
 #define PBA_DESC_OK          0
@@ -368,6 +369,30 @@ PBA_API int pba_packed_attn_bwd_stages(int stages, const pba_block_map* qmap, co
                                        const void* dout, void* dq, void* dk, void* dv, void* workspace,
                                        size_t workspace_bytes, int B, int S, int Hq, int Hkv, int D,
                                        float softmax_scale, void* stream);
+
+/* Backward without allocation, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  pba_packed_attn_bwd (both stages) with the caller's
+ * workspace replaced by a scratch array the library keeps in device memory:
+ * PBA_NOALLOC_SCRATCH_BYTES (96 MiB) on every device the library is used on,
+ * held from the library's load until the process ends.  The call itself
+ * allocates and frees nothing.  Arguments, results and errors are those of
+ * pba_packed_attn_bwd without the workspace, plus PBA_ERR_SCRATCH when the
+ * row statistics (two fp32 [B, Hq, S] arrays, i.e. 8 * B * Hq * S bytes,
+ * and one counter) do not fit the scratch.  The rest of the scratch holds
+ * the split key tiles' partial sums (256 KB per (key tile, kv head) pair at
+ * D = 128): when fewer pairs fit than pba_bwd_workspace_bytes provides
+ * for, fewer key tiles may be split, which changes only the rounding of
+ * their dK / dV; otherwise the results are bit-identical to
+ * pba_packed_attn_bwd's.  Every call on a device shares that device's
+ * scratch and finds it as the last call left it (the kernels overwrite or
+ * reset everything they read): calls that overlap on one device (two
+ * streams, or two threads on one stream without ordering) race. */
+#define PBA_NOALLOC_SCRATCH_BYTES (96u << 20)
+PBA_API int pba_packed_attn_bwd_noalloc(const pba_block_map* qmap, const pba_block_map* kmap, const void* q,
+                                        const void* k, const void* v, const void* o, const float* lse,
+                                        const void* dout, void* dq, void* dk, void* dv, int B, int S, int Hq,
+                                        int Hkv, int D, float softmax_scale, void* stream);
 
 /* Rounding of dK / dV and the compute-unit count.  A key tile whose visit
  * list is longer than 1.05 times the average load of one workgroup slot

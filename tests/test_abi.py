@@ -209,3 +209,32 @@ def test_traffic_records_from_counter_csv(tmp_path):
     assert rec["write_bytes_per_launch"] == 50 * 1024
     assert rec["sources_sha256"] == bench.sources_sha256(rec["sources"])
     assert json.load(open(tmp_path / "traffic_bwd_dkdv.json"))["read_bytes_per_launch"] == 2 * 2.0 * 1024
+
+
+def test_noalloc_backward_argument_errors():
+    """pba_packed_attn_bwd_noalloc checks its arguments as the workspace
+    entry point does, and refuses a problem whose row statistics do not fit
+    its fixed scratch, all before any device work."""
+    import block_sparse_attention_pack_amd as P
+    A = P.api
+    lib = A._lib
+    m, mb = A.PbaBlockMap(), A.PbaBlockMap()
+    assert lib.pba_map_init(ctypes.byref(m), 256, 1 << 20, 2, 100, 64, 64) == 0
+    assert lib.pba_map_init(ctypes.byref(mb), 256, 1 << 20, 2, 100, 64, 128) == 0
+    args = [ctypes.byref(m), ctypes.byref(mb)] + [16] * 9
+    assert lib.pba_packed_attn_bwd_noalloc(*([ctypes.byref(m), ctypes.byref(mb)] + [16] * 8 + [None]),
+                                           2, 100, 4, 2, 64, 0.1, None) == -1
+    assert lib.pba_packed_attn_bwd_noalloc(*args, 2, 101, 4, 2, 64, 0.1, None) == -6
+    assert lib.pba_packed_attn_bwd_noalloc(*args, 2, 100, 4, 4, 64, 0.1, None) == -5
+    assert lib.pba_packed_attn_bwd_noalloc(*args, 2, 100, 4, 2, 64, 0.0, None) == -10
+    assert lib.pba_packed_attn_bwd_noalloc(*args, 2, 100, 4, 2, 96, 0.1, None) == -4
+    # 16 rows of 32768 tokens x 32 q heads: 8 * B * Hq * S = 128 MiB of row
+    # statistics against the 96 MiB scratch
+    B, S = 16, 32768
+    big_q, big_k = A.PbaBlockMap(), A.PbaBlockMap()
+    assert lib.pba_map_init(ctypes.byref(big_q), 256, 1 << 40, B, S, *A.fwd_tile(32, 8, 128)) == 0
+    assert lib.pba_map_init(ctypes.byref(big_k), 256, 1 << 40, B, S, *A.bwd_tile(32, 8, 128)) == 0
+    big = [ctypes.byref(big_q), ctypes.byref(big_k)] + [16] * 9
+    assert 8 * B * 32 * S > A.NOALLOC_SCRATCH_BYTES
+    assert lib.pba_packed_attn_bwd_noalloc(*big, B, S, 32, 8, 128, 0.1, None) == -12
+    assert "scratch" in A.strerror(-12)
