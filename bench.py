@@ -305,6 +305,42 @@ def skip_cost(A, torch, steps, warmup, copy_gbps):
             "excess_frac": extra_ms / ts[ps.S]}
 
 
+def delta_pass(A, torch, r, ps, w, n=20):
+    """The row statistics of the backward ("LSE pass"): the forward writes
+    LSE (4 bytes per valid row and q head); the dQ kernel's prologue reads O
+    and dO (2 * 2 * D bytes per valid row and q head) and writes Delta =
+    rowsum(dO * O) and LSE * log2(e) (8 bytes).  It is fused into that
+    prologue, so it is timed as the dQ kernel on a copy of the map whose
+    query tiles visit no key tile: the prologue (Q, dO, O loads, Delta and
+    LSE2 stores) and a dQ block of zeros, nothing else.  GB/s = algorithmic
+    bytes of the pass / that time (an upper bound on its share of the
+    fused kernel's time, since Q's load and dQ's store are included)."""
+    m = A.BlockMap(ps.B, ps.S, *r.ftile)
+    nb = A.map_bytes(ps.B, ps.S, *r.ftile)
+    m.buffer[m._off0:m._off0 + nb].copy_(r.fmap.buffer[r.fmap._off0:r.fmap._off0 + nb])
+    m.q2k_cnt().zero_()
+    dq = torch.empty_like(r.dq)
+    run = lambda: A.packed_attn_bwd(m, r.bmap, r.q, r.k, r.v, r.o, r.lse, r.do, r.scale,  # noqa: E731
+                                    out=(dq, r.dk, r.dv), workspace=r.ws, stages=A.BWD_DQ)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    t_valid = ps.real_tokens()
+    alg = (2 * 2 * w.D + 8) * w.Hq * t_valid          # O, dO read; Delta, LSE2 written
+    moved = (3 * 2 * w.D + 4 + 8 + 2 * w.D) * w.Hq * ps.B * ps.S  # + Q, LSE read, dQ written, pad rows too
+    del m, dq
+    return {"fwd_lse_write_bytes": 4 * w.Hq * t_valid, "algorithmic_bytes": alg, "prologue_only_ms": ms,
+            "GBps": alg / (ms * 1e-3) / 1e9, "moved_bytes": moved, "moved_GBps": moved / (ms * 1e-3) / 1e9,
+            "frac_of_hbm_peak": alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
 def logp_rate(A, torch, r, pos_out, ps, V=151936):
     """Time pba_packed_token_logp on bf16 logits [B, S, V] (seeded normal,
     std 2.5) for the workload's response tokens: HBM bytes = one logits row
@@ -348,7 +384,7 @@ def cpu_baseline(w, seconds, gpu=None):
     P, R = descriptor_arrays(ps)
     pk, br, _ = oracle.token_ids(P, R, ps.B, ps.S)
     G = w.Hq // w.Hkv
-    flops, units, t_used = 0.0, [], 0.0
+    flops, dense, units, t_used = 0.0, 0.0, [], 0.0
     err = {"o_max_abs": 0.0, "lse_max_abs": 0.0}
     sq = {x: [0.0, 0.0] for x in ("o", "dq", "dk", "dv")}  # squared error, squared reference
     for b in range(ps.B):
@@ -375,6 +411,7 @@ def cpu_baseline(w, seconds, gpu=None):
                 lg, lr = gpu["lse"][b, h0:h1][:, valid].double(), L[b, h0:h1][:, valid]
                 err["lse_max_abs"] = max(err["lse_max_abs"], float((lg - lr).abs().max()))
             flops += 14.0 * w.D * G * n_allowed
+            dense += 14.0 * w.D * G * float(ps.S) ** 2
             units.append((b, g))
             if t_used >= seconds:
                 break
@@ -389,8 +426,10 @@ def cpu_baseline(w, seconds, gpu=None):
     except OSError:
         pass
     out = {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(), "kind": "oracle",
-           "sample": f"fp64 oracle fwd+bwd on {len(units)} of {ps.B * w.Hkv} (batch row, kv group) units "
-                     f"({G} q heads each) of the same workload, {t_used:.1f} s wall, useful-FLOP rate; CPU: {cpu}"}
+           "sample": f"{len(units)} of {ps.B * w.Hkv} (row, kv group) units, fp64 fwd+bwd, {t_used:.1f} s",
+           "cpu_model": cpu, "wall_s": t_used, "units": len(units), "units_total": ps.B * w.Hkv,
+           "dense_fp64_GFLOPs": dense / t_used / 1e9,
+           "dense_work_note": "14*D*G*S^2 per (row, kv group) unit: the oracle computes the whole masked S x S square"}
     if gpu is not None:
         err.update({f"{x}_rel_l2": (sq[x][0] / sq[x][1]) ** 0.5 if sq[x][1] > 0 else 0.0 for x in sq})
         out["parity_on_sample"] = err
@@ -563,20 +602,33 @@ def main():
     log(f"step {ms:.3f} ms  useful {value:.1f} TFLOP/s  per-kernel ms {json.dumps({k_: round(v_, 4) for k_, v_ in per.items()})}")
 
     # Useful FLOPs per allowed (query, key) pair and q head: 4*D forward,
-    # 10*D backward.  Per kernel, its own MFMA work on allowed pairs: the dQ
-    # kernel recomputes Q K^T and forms dO V^T and dS K (6*D), the dK/dV
-    # kernel recomputes Q K^T and dO V^T and forms P^T dO and dS^T Q (8*D).
-    per_pair = {"fwd": 4.0, "bwd_dq": 6.0, "bwd_dkdv": 8.0}
-    kern = {name: {"ms": per[name], "tflops_on_allowed_pairs": f * w.D * w.Hq * n_allowed / (per[name] * 1e-3) / 1e12,
-                   "flop_per_allowed_pair_per_head": f * w.D}
-            for name, f in per_pair.items()}
+    # 10*D backward (Q K^T again, dO V^T, P^T dO, dS^T Q, dS K).  Each
+    # backward kernel is credited only with work the other does not repeat:
+    # P^T dO and dS^T Q (4*D) are the dK/dV kernel's alone, dS K (2*D) the
+    # dQ kernel's alone, and Q K^T and dO V^T, which both form, count half
+    # to each (2*D each): 6*D for dK/dV, 4*D for dQ, 10*D together.  The MFMA
+    # work each kernel issues on allowed pairs (dK/dV 8*D, dQ 6*D, recomputed
+    # products included) is reported beside it.
+    credit = {"fwd": 4.0, "bwd_dq": 4.0, "bwd_dkdv": 6.0}
+    issued = {"fwd": 4.0, "bwd_dq": 6.0, "bwd_dkdv": 8.0}
+    rate = lambda f, t_ms: f * w.D * w.Hq * n_allowed / (t_ms * 1e-3) / 1e12  # noqa: E731
+    kern = {name: {"ms": per[name], "useful_tflops_credited": rate(credit[name], per[name]),
+                   "credited_flop_per_allowed_pair_per_head": credit[name] * w.D,
+                   "mfma_tflops_issued_on_allowed_pairs": rate(issued[name], per[name]),
+                   "issued_flop_per_allowed_pair_per_head": issued[name] * w.D}
+            for name in credit}
     kern["map"] = {"ms": per["map"], "GBps": (map_bytes(r, r.fmap) + map_bytes(r, r.bmap)) / (per["map"] * 1e-3) / 1e9}
-    dom = max(per_pair, key=lambda k_: per[k_])
-    achieved = kern[dom]["tflops_on_allowed_pairs"]
+    dom = max(credit, key=lambda k_: per[k_])
+    achieved = kern[dom]["useful_tflops_credited"]
     tr = traffic_record(dom)
+    t_pair = per["bwd_dq"] + per["bwd_dkdv"]
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": (tr["hbm_bytes_per_launch"] if tr else None)}
+                "traffic": (tr["hbm_bytes_per_launch"] if tr else None),
+                "credited_flop_per_allowed_pair_per_head": credit[dom] * w.D,
+                "frac_issued": kern[dom]["mfma_tflops_issued_on_allowed_pairs"] / PEAK_BF16_TFLOPS,
+                "frac_bwd_pair": rate(10.0, t_pair) / PEAK_BF16_TFLOPS,
+                "frac_fwd": rate(4.0, per["fwd"]) / PEAK_BF16_TFLOPS}
 
     extra = {"skip_frac_fwd_tiles": tot[2] / max(1, sum(tot)), "tiles_fwd": {"full": tot[0], "partial": tot[1], "skip": tot[2],
              "shape": list(r.ftile)},
@@ -603,6 +655,9 @@ def main():
             "pairwise_layout": {"B": pps.B, "S": pps.S, "allowed_pairs": allowed_pairs(pps)},
         })
         log(f"dense-map attn {att(per_d):.3f} ms, pairwise attn {att(per_p):.3f} ms, sparse attn {att(per):.3f} ms")
+
+    extra["lse_delta_pass"] = delta_pass(A, torch, r, ps, w)
+    log(f"lse / delta pass: {json.dumps(extra['lse_delta_pass'])}")
 
     # Aligned positions / log-prob gather rows (a next step on the same map, reported beside the step).
     pos_out = (torch.empty((ps.B, ps.S), dtype=torch.int32, device=dev),
