@@ -464,11 +464,18 @@ __device__ __forceinline__ void part_add(f32x16 (&acc)[D / 32], const float* p, 
     }
 }
 
-// 8 waves, 128 keys: wave w owns keys 32*(w%4) .. +31 and the query half
-// w/4 of every 64-query step.  K and V of the 128 keys stay in LDS for the
-// whole kernel (B operands read per step); Q, dO, LSE2 and Delta tiles are
-// staged by direct loads into a double buffer.  The two waves that share
-// keys sum their partial dK / dV through LDS at the end.
+// 8 waves, 128 keys: wave w owns the query half qh = w/4 of every 64-query
+// step and the key block kb (keys 32*kb .. +31) with kb = w%4 for qh = 0 and
+// kb = 3 - w%4 for qh = 1.  Waves w and w+4 share a SIMD, so a SIMD pairs
+// the sub-blocks (kb, 0) and (3-kb, 1): on a tile across the causal
+// diagonal the fully masked sub-blocks (keys after every query of the
+// half) fall on different SIMDs than the live ones, and a wave whose
+// sub-block of a partial tile is fully masked skips that step's arithmetic
+// (its contribution is exactly zero), leaving its SIMD to the other wave.
+// K and V of the 128 keys stay in LDS for the whole kernel (B operands read
+// per step); Q, dO, LSE2 and Delta tiles are staged by direct loads into a
+// double buffer.  The two waves that share keys sum their partial dK / dV
+// through LDS at the end.
 template <int D>
 __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   using C = BwdCfg<D>;
@@ -490,7 +497,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
-  const int kb = w & 3, qh = w >> 2;  // key block, query half
+  const int qh = w >> 2, kb = qh ? 3 - (w & 3) : (w & 3);  // query half, key block
   const int Hkv = a.Hkv, G = a.G, S = a.S, Hq = a.Hq;
   // Workgroup slots: with K split positions (counted by bwd_dq), the first
   // 2K slots take the two halves of the first K work-order positions, the
@@ -563,14 +570,20 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   // Full query tiles come first in the list, then partial ones; a loop for
   // each keeps the dK / dV accumulators in place.
   auto visit = [&](int i, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int qt = min(max(list[i], 0), mp.nqt - 1);
     const int qrel = kj - qt * 64, qlim = qend - kj;
+    // On a partial tile, this wave's 32 x 32 sub-block is live iff some key
+    // of it is seen by some query of its half: key kj is seen by tile rows
+    // [qrel, qrel + qlim).
+    const bool live = !MASKED || __builtin_amdgcn_ballot_w64(qlim > 0 && qrel < 32 * qh + 32 && qrel + qlim > 32 * qh);
     for (int hh = 0; hh < G; ++hh) {
       // Prefetch the next step into the other buffer (last read one step ago).
       if (hh + 1 < G) stage(i, hh + 1, buf ^ 1);
       else if (i + 1 < i1) stage(i + 1, 0, buf ^ 1);
-      dkdv_step<D, decltype(masked)::value>(dkt, dvt, skp, svp, 32 * kb, sQ[buf], sDO[buf], sL[buf], sD[buf], 32 * qh,
-                                            a.scale_log2, qrel, qlim, lane);
+      if (live)
+        dkdv_step<D, MASKED>(dkt, dvt, skp, svp, 32 * kb, sQ[buf], sDO[buf], sL[buf], sD[buf], 32 * qh, a.scale_log2,
+                             qrel, qlim, lane);
       wait_vmem();
       __syncthreads();
       buf ^= 1;
