@@ -543,14 +543,28 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
     kst.stage(sK, a.k + koff, S - kt * 128);
     kst.stage(sV, a.v + koff, S - kt * 128);
   }
-  auto stage = [&](int i, int hh, int buf) {
-    const int qt = min(max(list[i], 0), mp.nqt - 1), h = g * G + hh;
-    const int64_t toff = ((int64_t)b * S + qt * 64) * qstride + (int64_t)h * D;
-    qst.stage(sQ[buf], a.q + toff, S - qt * 64);
-    qst.stage(sDO[buf], a.dout + toff, S - qt * 64);
-    const int64_t roff = ((int64_t)b * Hq + h) * S + qt * 64;
-    if (w == 0) buffer_lds_dword(a.lse2 + roff, S - qt * 64, &sL[buf][0], lane4);
-    if (w == 1) buffer_lds_dword(a.delta + roff, S - qt * 64, &sD[buf][0], lane4);
+  // Staging addresses of one query tile for the group's first q head; the
+  // other heads are D elements (Q, dO) or S floats (LSE2, Delta) further.
+  // Computed once per query tile: a step only offsets the bases.
+  struct TileAddr {
+    const bf16* q;
+    const bf16* dout;
+    const float* l2;
+    const float* delta;
+    int rows;  // valid rows from the tile's first on (rows past S read as zeros)
+  };
+  const int64_t qrow0 = (int64_t)b * S * qstride + (int64_t)(g * G) * D;
+  const int64_t lrow0 = ((int64_t)b * Hq + g * G) * S;
+  auto tile_addr = [&](int qt) {
+    const int r0 = qt * 64;
+    const int64_t o = qrow0 + (int64_t)r0 * qstride;
+    return TileAddr{a.q + o, a.dout + o, a.lse2 + lrow0 + r0, a.delta + lrow0 + r0, S - r0};
+  };
+  auto stage = [&](const TileAddr& t, int hh, int buf) {
+    qst.stage(sQ[buf], t.q + hh * D, t.rows);
+    qst.stage(sDO[buf], t.dout + hh * D, t.rows);
+    if (w == 0) buffer_lds_dword(t.l2 + hh * S, t.rows, &sL[buf][0], lane4);
+    if (w == 1) buffer_lds_dword(t.delta + hh * S, t.rows, &sD[buf][0], lane4);
   };
 
   f32x16 dkt[C::NE], dvt[C::NE];
@@ -563,7 +577,9 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   // every outstanding global->LDS load, i.e. for the next step's tiles).
   const bf16* skp = opaque_lds(sK);
   const bf16* svp = opaque_lds(sV);
-  if (i1 > i0) stage(i0, 0, 0);
+  auto tile_of = [&](int i) { return min(max(list[i], 0), mp.nqt - 1); };
+  int qt_cur = tile_of(i0);  // valid memory even for an empty list
+  if (i1 > i0) stage(tile_addr(qt_cur), 0, 0);
   wait_vmem();
   __syncthreads();
   int buf = 0;
@@ -571,7 +587,10 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   // each keeps the dK / dV accumulators in place.
   auto visit = [&](int i, auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
-    const int qt = min(max(list[i], 0), mp.nqt - 1);
+    const int qt = qt_cur;
+    // The next tile's list entry and addresses, read once per tile.
+    const int qt_next = i + 1 < i1 ? tile_of(i + 1) : qt;
+    const TileAddr cur = tile_addr(qt), nxt = tile_addr(qt_next);
     const int qrel = kj - qt * 64, qlim = qend - kj;
     // On a partial tile, this wave's 32 x 32 sub-block is live iff some key
     // of it is seen by some query of its half: key kj is seen by tile rows
@@ -579,8 +598,8 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
     const bool live = !MASKED || __builtin_amdgcn_ballot_w64(qlim > 0 && qrel < 32 * qh + 32 && qrel + qlim > 32 * qh);
     for (int hh = 0; hh < G; ++hh) {
       // Prefetch the next step into the other buffer (last read one step ago).
-      if (hh + 1 < G) stage(i, hh + 1, buf ^ 1);
-      else if (i + 1 < i1) stage(i + 1, 0, buf ^ 1);
+      if (hh + 1 < G) stage(cur, hh + 1, buf ^ 1);
+      else if (i + 1 < i1) stage(nxt, 0, buf ^ 1);
       if (live)
         dkdv_step<D, MASKED>(dkt, dvt, skp, svp, 32 * kb, sQ[buf], sDO[buf], sL[buf], sD[buf], 32 * qh, a.scale_log2,
                              qrel, qlim, lane);
@@ -588,6 +607,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
       __syncthreads();
       buf ^= 1;
     }
+    qt_cur = qt_next;
   };
   int i = i0;
   for (; i < min(nfull, i1); ++i) visit(i, std::false_type{});

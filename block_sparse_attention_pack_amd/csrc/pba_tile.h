@@ -206,14 +206,19 @@ struct Stager {
   // this, must not instantiate it or it drops the kernels' host stubs.)
   __device__ __forceinline__ void stage(bf16* lds_tile, const bf16* tile, int rows) const {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const __amdgpu_buffer_rsrc_t rs = rows_rsrc(tile, rows, row_stride, D);
+    stage_rs(lds_tile, rows_rsrc(tile, rows, row_stride, D));
+#endif
+  }
+  // The same from a resource built by the caller (rows_rsrc of the tile).
+#if defined(__HIP_DEVICE_COMPILE__)
+  __device__ __forceinline__ void stage_rs(bf16* lds_tile, __amdgpu_buffer_rsrc_t rs) const {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int q = w * PER_WAVE + i;
       if (q < NI) dma_to_lds<16>(rs, lds_tile + 512 * q, off[i]);
     }
-#endif
   }
+#endif
 };
 
 // A workgroup's block of R rows x RB bytes that are contiguous within a row
