@@ -200,39 +200,41 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   char* const pair1 = (char*)(lds + 2 * T);   // K(1) V(1)
   const int qrows = min(R, S - q0), qrow_bytes = Hq * D * 2;
   const int64_t blk = ((int64_t)b * S + q0) * Hq * D + (int64_t)h0 * D;
-  Blk::template load<4>(pair1, a.q + blk, qrows, qrow_bytes, w, lane);
-  Blk::template load<4>(pair0, a.dout + blk, qrows, qrow_bytes, w, lane);
   const int first = list[0];  // valid memory even for an empty list
   const int4 wv = reinterpret_cast<const int4*>(mp.tok_win)[(int64_t)b * S + qc];
   const float lse = a.lse[((int64_t)b * Hq + h) * S + qc];
-  wait_vmem();
-  __syncthreads();
   // Q^T and dO^T as B operands: lane holds query qi, head dims 16*st + 8*hi + 0..7.
   bf16x8 qop[C::NS], dop[C::NS];
-  const int rofs = (qb * 32 + l32) * Blk::LSTR + hw * D * 2 + 16 * hi;
-#pragma unroll
-  for (int st = 0; st < C::NS; ++st) {
-    qop[st] = *(const bf16x8*)(pair1 + rofs + 32 * st);
-    dop[st] = *(const bf16x8*)(pair0 + rofs + 32 * st);
-  }
-  __syncthreads();
+  float delta = 0.f;
+  // A query tile that visits no key tile holds only pad rows, whose dQ,
+  // Delta and LSE2 are all 0: its row blocks are not read at all.
   if (n > 0) {
+    Blk::template load<4>(pair1, a.q + blk, qrows, qrow_bytes, w, lane);
+    Blk::template load<4>(pair0, a.dout + blk, qrows, qrow_bytes, w, lane);
+    wait_vmem();
+    __syncthreads();
+    const int rofs = (qb * 32 + l32) * Blk::LSTR + hw * D * 2 + 16 * hi;
+#pragma unroll
+    for (int st = 0; st < C::NS; ++st) {
+      qop[st] = *(const bf16x8*)(pair1 + rofs + 32 * st);
+      dop[st] = *(const bf16x8*)(pair0 + rofs + 32 * st);
+    }
+    __syncthreads();
     const int k0 = min(max(first, 0), mp.nkt - 1) * 64;
     kst.stage(sK(0), kb + (int64_t)k0 * kvstride, S - k0);
     kst.stage(sV(0), vb + (int64_t)k0 * kvstride, S - k0);
-  }
-  Blk::template load<4>(pair1, a.o + blk, qrows, qrow_bytes, w, lane);
-  wait_vmem();
-  __syncthreads();
-  // Delta = rowsum(dO * O) from the same lanes.
-  float delta = 0.f;
+    Blk::template load<4>(pair1, a.o + blk, qrows, qrow_bytes, w, lane);
+    wait_vmem();
+    __syncthreads();
+    // Delta = rowsum(dO * O) from the same lanes.
 #pragma unroll
-  for (int st = 0; st < C::NS; ++st) {
-    const bf16x8 ov = *(const bf16x8*)(pair1 + rofs + 32 * st);
+    for (int st = 0; st < C::NS; ++st) {
+      const bf16x8 ov = *(const bf16x8*)(pair1 + rofs + 32 * st);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) delta += (float)dop[st][t] * (float)ov[t];
+      for (int t = 0; t < 8; ++t) delta += (float)dop[st][t] * (float)ov[t];
+    }
+    delta += wave_half_swap(delta);
   }
-  delta += wave_half_swap(delta);
   const int wlo = qi < S ? wv.x : qi + 1, wplo = qi < S ? wv.y : 0, wphi = qi < S ? wv.z : 0;
   // log2-domain LSE; a row that sees no key (LSE = -inf) is masked on every
   // tile it meets, and 0 keeps its arithmetic finite.
@@ -538,7 +540,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   const Stager<D, C::STR, 64, 8> qst(tid, qstride);    // Q and dO
   int lane4 = lane * 4;
   pin(lane4);
-  {
+  if (i1 > i0) {  // (a key tile no query visits holds pad keys only: dK = dV = 0)
     const int64_t koff = ((int64_t)b * S + kt * 128) * kvstride + (int64_t)g * D;
     kst.stage(sK, a.k + koff, S - kt * 128);
     kst.stage(sV, a.v + koff, S - kt * 128);

@@ -275,8 +275,11 @@ __global__ void __launch_bounds__(256, 2) fwd_kernel(FwdArgs a) {
   auto sV = [&](int t) { return lds + (2 + (t & 1)) * T; };  // V of visit t
   auto key0 = [&](int t) { return min(max(list[t], 0), mp.nkt - 1) * 64; };
 
-  // Prologue: the Q block and the first two K tiles, all as direct loads.
-  Blk::template load<4>(q_lds, a.q + ((int64_t)b * S + q0) * Hq * D + (int64_t)h0 * D, qrows, qrow_bytes, w, lane);
+  // Prologue: the Q block and the first two K tiles, all as direct loads.  A
+  // query tile that visits no key tile holds only pad rows (O = 0, LSE =
+  // -inf): its Q block is read only when the rotated Q is to be written.
+  if (n > 0 || (ROPE && a.q_rot))
+    Blk::template load<4>(q_lds, a.q + ((int64_t)b * S + q0) * Hq * D + (int64_t)h0 * D, qrows, qrow_bytes, w, lane);
   const int first = list[0];  // valid memory even for an empty list
   asm volatile("" ::"s"(first), "s"(n));
   if (n > 0) {
