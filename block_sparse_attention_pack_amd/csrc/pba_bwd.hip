@@ -10,8 +10,9 @@
 //   bwd_dq    query-major, on the map of the forward's tile shape.  A
 //             workgroup = one query tile x WGH q heads of one kv group, one
 //             wave = 32 queries of one head.  Its prologue stages the Q and
-//             dO blocks, then the O block with the first K/V tile, forms
-//             Delta = rowsum(dO * O) and writes Delta and the log2-domain LSE
+//             dO blocks (O straight into registers), forms
+//             Delta = rowsum(dO * O), then stages the first K/V tile; it
+//             writes Delta and the log2-domain LSE
 //             (0 where the row sees nothing) for bwd_dkdv; then it walks the
 //             query tile's key tiles: S^T = K Q^T, dP^T = V dO^T, dS^T,
 //             dQ^T += K^T dS^T, the two 32-key halves of a tile staggered.
@@ -193,9 +194,9 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   const bf16* vb = a.v + ((int64_t)b * S * Hkv + g) * D;
   const Stager<D, C::STR> kst(tid, kvstride);  // K and V tiles have the same shape
 
-  // Prologue in two rounds of direct (whole-row) loads, as the three row
-  // blocks and the first K/V tile do not fit in LDS at once: Q and dO into
-  // the two buffer pairs, then O and the first K/V tile.
+  // Prologue in two rounds, as the Q and dO blocks and the first K/V tile do
+  // not fit in LDS at once: Q and dO into the two buffer pairs (with O into
+  // registers), then the first K/V tile.
   char* const pair0 = (char*)lds;             // K(0) V(0)
   char* const pair1 = (char*)(lds + 2 * T);   // K(1) V(1)
   const int qrows = min(R, S - q0), qrow_bytes = Hq * D * 2;
@@ -209,8 +210,23 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   // A query tile that visits no key tile holds only pad rows, whose dQ,
   // Delta and LSE2 are all 0: its row blocks are not read at all.
   if (n > 0) {
+    // Round 1: the Q and dO blocks into the two buffer pairs (whole-row
+    // direct loads) and, at the same time, this lane's O chunks straight into
+    // registers, in the lane layout of the dO operand (query row qi, head dims
+    // 16*st + 8*hi + 0..7): O is needed only for Delta.  Rows past S read as
+    // zeros through the resource's range.
     Blk::template load<4>(pair1, a.q + blk, qrows, qrow_bytes, w, lane);
     Blk::template load<4>(pair0, a.dout + blk, qrows, qrow_bytes, w, lane);
+    u32x4 ov[C::NS];
+    {
+      const int r0 = q0 + qb * 32, nrows = min(32, S - r0);
+      const bf16* orow = a.o + ((int64_t)b * S + r0) * Hq * D + (int64_t)h * D;
+      const int nbytes = nrows > 0 ? ((nrows - 1) * Hq * D + D) * 2 : 0;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)orow, (short)0, nbytes, 0x00020000);
+      const int voff = (l32 * Hq * D + 8 * hi) * 2;
+#pragma unroll
+      for (int st = 0; st < C::NS; ++st) ov[st] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 32 * st, 0, 0);
+    }
     wait_vmem();
     __syncthreads();
     const int rofs = (qb * 32 + l32) * Blk::LSTR + hw * D * 2 + 16 * hi;
@@ -219,21 +235,22 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
       qop[st] = *(const bf16x8*)(pair1 + rofs + 32 * st);
       dop[st] = *(const bf16x8*)(pair0 + rofs + 32 * st);
     }
-    __syncthreads();
-    const int k0 = min(max(first, 0), mp.nkt - 1) * 64;
-    kst.stage(sK(0), kb + (int64_t)k0 * kvstride, S - k0);
-    kst.stage(sV(0), vb + (int64_t)k0 * kvstride, S - k0);
-    Blk::template load<4>(pair1, a.o + blk, qrows, qrow_bytes, w, lane);
-    wait_vmem();
-    __syncthreads();
     // Delta = rowsum(dO * O) from the same lanes.
 #pragma unroll
     for (int st = 0; st < C::NS; ++st) {
-      const bf16x8 ov = *(const bf16x8*)(pair1 + rofs + 32 * st);
+      const bf16x8 o8 = __builtin_bit_cast(bf16x8, ov[st]);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) delta += (float)dop[st][t] * (float)ov[t];
+      for (int t = 0; t < 8; ++t) delta += (float)dop[st][t] * (float)o8[t];
     }
     delta += wave_half_swap(delta);
+    __syncthreads();
+    // Round 2: the first K/V tile (shared with other query tiles, so mostly
+    // a cache hit).
+    const int k0 = min(max(first, 0), mp.nkt - 1) * 64;
+    kst.stage(sK(0), kb + (int64_t)k0 * kvstride, S - k0);
+    kst.stage(sV(0), vb + (int64_t)k0 * kvstride, S - k0);
+    wait_vmem();
+    __syncthreads();
   }
   const int wlo = qi < S ? wv.x : qi + 1, wplo = qi < S ? wv.y : 0, wphi = qi < S ? wv.z : 0;
   // log2-domain LSE; a row that sees no key (LSE = -inf) is masked on every
@@ -243,7 +260,6 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   f32x16 dq[C::NE];
 #pragma unroll
   for (int e = 0; e < C::NE; ++e) dq[e] = f32x16{};
-  __syncthreads();  // the O block has been read: the second pair is free
   // One visit: the next tile's loads go into the other buffer, then this
   // tile's math.  Full tiles precede partial ones in the list; a loop for
   // each keeps the dQ accumulators in place (two paths merging inside one
