@@ -426,8 +426,8 @@ size_t pba_bwd_workspace_bytes(int B, int S, int Hq, int D) {
 }  // extern "C"
 
 namespace {
-// Bytes of the backward's scratch with `pairs` split pairs: Delta and LSE2
-// (fp32 [B, Hq, S] each), pairs + 1 arrival counters, the partial sums.
+// Bytes of the backward's scratch with `pairs` split pairs: -Delta and
+// -LSE / scale (fp32 [B, Hq, S] each), pairs + 1 arrival counters, the partial sums.
 size_t bwd_scratch_bytes(int B, int S, int Hq, int D, size_t pairs) {
   return 2 * align_up((size_t)B * Hq * S * 4) + align_up((pairs + 1) * 4) + pairs * 2 * 2 * pba::kBwdBN * D * 4;
 }
@@ -470,8 +470,8 @@ int bwd_launch(int stages, const pba_block_map* qmap, const pba_block_map* kmap,
   a.dq = static_cast<pba::bf16*>(dq);
   a.dk = static_cast<pba::bf16*>(dk);
   a.dv = static_cast<pba::bf16*>(dv);
-  a.delta = static_cast<float*>(ws);
-  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)B * Hq * S * 4));
+  a.dp0 = static_cast<float*>(ws);
+  a.s0 = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)B * Hq * S * 4));
   a.B = B;
   a.S = S;
   a.Hq = Hq;
@@ -528,9 +528,9 @@ void* scratch_address() {
   return addr[dev];
 }
 
-// Split pairs that fit the scratch next to Delta and LSE2 (at most the
+// Split pairs that fit the scratch next to the per-row arrays (at most the
 // workspace's own count, so results match pba_packed_attn_bwd whenever they
-// all fit); -1 when Delta, LSE2 and one counter alone do not fit.
+// all fit); -1 when those arrays and one counter alone do not fit.
 long long noalloc_pairs(int B, int S, int Hq, int D) {
   size_t pairs = split_pairs(B, S, Hq);
   if (bwd_scratch_bytes(B, S, Hq, D, 0) > PBA_NOALLOC_SCRATCH_BYTES) return -1;

@@ -12,14 +12,15 @@
 //             wave = 32 queries of one head.  Its prologue stages the Q and
 //             dO blocks (O straight into registers), forms
 //             Delta = rowsum(dO * O), then stages the first K/V tile; it
-//             writes Delta and the log2-domain LSE
-//             (0 where the row sees nothing) for bwd_dkdv; then it walks the
+//             writes -Delta and -LSE / scale (0 where the row sees nothing)
+//             for bwd_dkdv; then it walks the
 //             query tile's key tiles: S^T = K Q^T, dP^T = V dO^T, dS^T,
 //             dQ^T += K^T dS^T, the two 32-key halves of a tile staggered.
 //   bwd_dkdv  key-major, on a map with 64-query x 128-key tiles.  A
 //             workgroup = one key tile x one kv group, 8 waves (32 keys x one
 //             32-query half each); K and V of the 128 keys stay in LDS, a
-//             wave's dK^T / dV^T in registers.  It walks the key tile's query
+//             wave's K operands, dK^T and dV^T in registers.  It walks the key
+//             tile's query
 //             tiles and, for each q head of the group, S = Q K^T, dP = dO V^T,
 //             dV^T += dO^T P, dK^T += Q^T dS, summing over the group's heads;
 //             the two query halves' partial sums meet in LDS at the end.
@@ -286,11 +287,12 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   for (; j < nfull; ++j) visit(j, std::false_type{});
   for (; j < n; ++j) visit(j, std::true_type{});
 
-  // (Delta and LSE2 are stored only now: a store still in flight when the
-  // loop reuses its data registers would make every tile wait for memory.)
+  // For bwd_dkdv, the starting values of its dP and score accumulators
+  // (stored only now: a store still in flight when the loop reuses its data
+  // registers would make every tile wait for memory).
   if (qi < S && hi == 0) {
-    a.delta[((int64_t)b * Hq + h) * S + qi] = delta;
-    a.lse2[((int64_t)b * Hq + h) * S + qi] = l2;
+    a.dp0[((int64_t)b * Hq + h) * S + qi] = -delta;
+    a.s0[((int64_t)b * Hq + h) * S + qi] = -l2 / a.scale_log2;
   }
   // With rotary inputs, dQ is rotated back to the unrotated Q's frame at
   // the query's packed position (its row is 0 where the query is pad).
@@ -321,21 +323,24 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
 
 // One (query tile, q head) step for one wave of bwd_dkdv: one 32-query half
 // of the 64-query tile (rows q0 .. q0+31 of the staged tiles) x the wave's
-// 32 keys (rows k0 .. k0+31 of the resident K / V tiles).  Query
-// q0 + 8*(r/4) + 4*hi + r%4 sits in register r of s.  On partial tiles
+// 32 keys (K operands in registers, rows k0 .. k0+31 of the resident V
+// tile).  Query q0 + 8*(r/4) + 4*hi + r%4 sits in register r of s.  The
+// score and dP accumulators start from -LSE / scale and -Delta (staged
+// per row in s0 and dp0), so they finish as S - LSE / scale, whose
+// exp2(scale_log2 * x) is P, and dP - Delta: no per-score subtraction.  On partial tiles
 // (MASK) the lane's key kj is seen by queries [kj, qend): row index x of the
 // tile is visible iff (unsigned)(x - qrel) < (unsigned)qlim (qrel = kj - the
 // tile's first query, qlim = qend - kj).  These compares depend on the tile
 // only, so the compiler keeps them in scalar lane masks across the q heads.
 template <int D, bool MASK>
-__device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D / 32], const bf16* __restrict__ sk,
+__device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D / 32], const bf16x8 (&kop)[D / 16],
                                           const bf16* __restrict__ sv, int k0, const bf16* __restrict__ sq,
-                                          const bf16* __restrict__ sdo, const float* __restrict__ sl,
-                                          const float* __restrict__ sd, int q0, float scale_log2, int qrel,
+                                          const bf16* __restrict__ sdo, const float* __restrict__ s0,
+                                          const float* __restrict__ dp0, int q0, float scale_log2, int qrel,
                                           int qlim, int lane) {
   using C = BwdCfg<D>;
-  // Hand-scheduled: the S / dP MFMAs (A = Q / dO rows, B = K / V rows, both
-  // from LDS), the vector work of query rows 0-15 of the 32 (registers 0-7),
+  // Hand-scheduled: the S / dP MFMAs (A = Q / dO rows from LDS, B = the K
+  // operands in registers / V rows from LDS), the vector work of query rows 0-15 of the 32 (registers 0-7),
   // then the dV / dK MFMAs of those rows with the vector work of rows 16-31
   // between them, then the dV / dK MFMAs of rows 16-31.  Operand reads run
   // two MFMAs ahead.
@@ -350,22 +355,32 @@ __device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D
       const int qo = prow(q0 + l32) * C::STR + 16 * st + 8 * hi;
       const int ko = prow(k0 + l32) * C::STR + 16 * st + 8 * hi;
       return (i & 1) ? Ops{*(const bf16x8*)(sdo + qo), *(const bf16x8*)(sv + ko)}
-                     : Ops{*(const bf16x8*)(sq + qo), *(const bf16x8*)(sk + ko)};
+                     : Ops{*(const bf16x8*)(sq + qo), kop[st]};
     }
     const int k = i - NSD, u = k / NG, e = (k % NG) >> 1;  // dV (even) / dK (odd) of row half u
     const int r0 = q0 + 16 * u + 4 * hi;
     return Ops{lds_tr8p((k & 1) ? sq : sdo, C::STR, r0, r0 + 8, 32 * e, lane), bf16x8{}};
   };
-  f32x16 s = f32x16{}, dp = f32x16{};
-  f32x4 lv[4], dv[4];
+  f32x16 s, dp;
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg) {
+    const int qr = q0 + 8 * rg + 4 * hi;
+    const f32x4 l = *(const f32x4*)(s0 + qr);
+    const f32x4 d = *(const f32x4*)(dp0 + qr);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      s[4 * rg + t] = l[t];
+      dp[4 * rg + t] = d[t];
+    }
+  }
   bf16x8 pb[2], db[2];
   // Score r (register r: query row q0 + 8*(r/4) + 4*hi + r%4).
   auto score = [&](int r) __attribute__((always_inline)) {
     const int rg = r >> 2, t = r & 3;
-    float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -lv[rg][t]));
+    float p = fast_exp2(s[r] * scale_log2);
     if (MASK) p = (unsigned)(q0 + 8 * rg + 4 * hi + t - qrel) < (unsigned)qlim ? p : 0.f;
     s[r] = p;
-    dp[r] = p * (dp[r] - dv[rg][t]);
+    dp[r] = p * dp[r];
   };
   Ops ops[3];
   ops[0] = operand(0);
@@ -377,11 +392,6 @@ __device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D
     if constexpr (i < NSD) {
       if constexpr (i & 1) dp = mfma32(ops[i % 3].a, ops[i % 3].b, dp);
       else s = mfma32(ops[i % 3].a, ops[i % 3].b, s);
-      if constexpr (i < 4) {  // LSE2 / Delta of the four row groups
-        const int qr = q0 + 8 * i + 4 * hi;
-        lv[i] = *(const f32x4*)(sl + qr);
-        dv[i] = *(const f32x4*)(sd + qr);
-      }
       if constexpr (i == NSD - 1) {
         sched_fence();
 #pragma unroll
@@ -490,9 +500,10 @@ __device__ __forceinline__ void part_add(f32x16 (&acc)[D / 32], const float* p, 
 // half) fall on different SIMDs than the live ones, and a wave whose
 // sub-block of a partial tile is fully masked skips that step's arithmetic
 // (its contribution is exactly zero), leaving its SIMD to the other wave.
-// K and V of the 128 keys stay in LDS for the whole kernel (B operands read
-// per step); Q, dO, LSE2 and Delta tiles are staged by direct loads into a
-// double buffer.  The two waves that share keys sum their partial dK / dV
+// K and V of the 128 keys are staged once: each wave reads its 32 keys' K
+// operands (B operands of S) into registers, while V stays in LDS (B
+// operands of dP, read per step); Q, dO and the 64 rows' -LSE / scale and
+// -Delta are staged by direct loads into a double buffer.  The two waves that share keys sum their partial dK / dV
 // through LDS at the end.
 template <int D>
 __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
@@ -507,7 +518,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16 sQ[2][TQ];
   __shared__ __attribute__((aligned(1024))) bf16 sDO[2][TQ];
   static_assert(2 * TQ * sizeof(bf16) >= 2 * 64 * (D / 2 + 4) * sizeof(float), "exchange must fit a staging array");
-  __shared__ __attribute__((aligned(16))) float sL[2][64], sD[2][64];
+  __shared__ __attribute__((aligned(16))) float sS0[2][64], sDP0[2][64];
   __shared__ int s_second;  // this workgroup is the second half of a split key tile to finish
 
   const MapView& mp = a.kmap;
@@ -562,13 +573,13 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
     kst.stage(sV, a.v + koff, S - kt * 128);
   }
   // Staging addresses of one query tile for the group's first q head; the
-  // other heads are D elements (Q, dO) or S floats (LSE2, Delta) further.
+  // other heads are D elements (Q, dO) or S floats (s0, dp0) further.
   // Computed once per query tile: a step only offsets the bases.
   struct TileAddr {
     const bf16* q;
     const bf16* dout;
-    const float* l2;
-    const float* delta;
+    const float* s0;
+    const float* dp0;
     int rows;  // valid rows from the tile's first on (rows past S read as zeros)
   };
   const int64_t qrow0 = (int64_t)b * S * qstride + (int64_t)(g * G) * D;
@@ -576,13 +587,13 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   auto tile_addr = [&](int qt) {
     const int r0 = qt * 64;
     const int64_t o = qrow0 + (int64_t)r0 * qstride;
-    return TileAddr{a.q + o, a.dout + o, a.lse2 + lrow0 + r0, a.delta + lrow0 + r0, S - r0};
+    return TileAddr{a.q + o, a.dout + o, a.s0 + lrow0 + r0, a.dp0 + lrow0 + r0, S - r0};
   };
   auto stage = [&](const TileAddr& t, int hh, int buf) {
     qst.stage(sQ[buf], t.q + hh * D, t.rows);
     qst.stage(sDO[buf], t.dout + hh * D, t.rows);
-    if (w == 0) buffer_lds_dword(t.l2 + hh * S, t.rows, &sL[buf][0], lane4);
-    if (w == 1) buffer_lds_dword(t.delta + hh * S, t.rows, &sD[buf][0], lane4);
+    if (w == 0) buffer_lds_dword(t.s0 + hh * S, t.rows, &sS0[buf][0], lane4);
+    if (w == 1) buffer_lds_dword(t.dp0 + hh * S, t.rows, &sDP0[buf][0], lane4);
   };
 
   f32x16 dkt[C::NE], dvt[C::NE];
@@ -601,6 +612,11 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   wait_vmem();
   __syncthreads();
   int buf = 0;
+  // This wave's K operands (the B operands of S = Q K^T), read once.
+  bf16x8 kop[C::NS];
+#pragma unroll
+  for (int st = 0; st < C::NS; ++st)
+    kop[st] = *(const bf16x8*)(skp + prow(32 * kb + l32) * C::STR + 16 * st + 8 * (lane >> 5));
   // Full query tiles come first in the list, then partial ones; a loop for
   // each keeps the dK / dV accumulators in place.
   auto visit = [&](int i, auto masked) {
@@ -619,8 +635,8 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
       if (hh + 1 < G) stage(cur, hh + 1, buf ^ 1);
       else if (i + 1 < i1) stage(nxt, 0, buf ^ 1);
       if (live)
-        dkdv_step<D, MASKED>(dkt, dvt, skp, svp, 32 * kb, sQ[buf], sDO[buf], sL[buf], sD[buf], 32 * qh, a.scale_log2,
-                             qrel, qlim, lane);
+        dkdv_step<D, MASKED>(dkt, dvt, kop, svp, 32 * kb, sQ[buf], sDO[buf], sS0[buf], sDP0[buf], 32 * qh,
+                             a.scale_log2, qrel, qlim, lane);
       wait_vmem();
       __syncthreads();
       buf ^= 1;

@@ -65,8 +65,11 @@ struct BwdArgs {
   bf16* dq;
   bf16* dk;
   bf16* dv;
-  float* delta;  // [B, Hq, S] fp32 rowsum(dO * O), written by bwd_dq
-  float* lse2;   // [B, Hq, S] fp32 LSE * log2(e) (0 for rows that see nothing)
+  // Written by bwd_dq for bwd_dkdv: the values its dP and score
+  // accumulators start from, so that the finished accumulators are dP - Delta
+  // and S - LSE / scale (whose exp2(scale * log2(e) * x) is P).
+  float* dp0;  // [B, Hq, S] fp32 -Delta = -rowsum(dO * O)
+  float* s0;   // [B, Hq, S] fp32 -LSE / scale (0 for rows that see nothing)
   int B, S, Hq, Hkv, G;
   float scale, scale_log2;
   // log2 of the rotary base when dQ and dK are rotated back to the
