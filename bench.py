@@ -660,6 +660,22 @@ def main():
         })
         log(f"dense-map attn {att(per_d):.3f} ms, pairwise attn {att(per_p):.3f} ms, sparse attn {att(per):.3f} ms")
 
+    if not args.no_baselines:
+        # Context only: the same step once the device has run it for a
+        # while.  A fresh process runs its first ~60 steps up to 15% slower
+        # (other load beforehand does not remove this, only the step itself
+        # does), so `value` above, taken after W warm-up steps, sits on that
+        # ramp.
+        t_ss = time.perf_counter()
+        while time.perf_counter() - t_ss < 0.4:
+            r.step()
+            torch.cuda.synchronize()
+        ms_ss, per_ss = time_runner(torch, r, args.steps, 0)
+        extra["steady_state"] = {"after_seconds_of_steps": 0.4, "ms_per_step": ms_ss,
+                                 "useful_tflops": useful / (ms_ss * 1e-3) / 1e12,
+                                 "kernels_ms": {k_: round(v_, 4) for k_, v_ in per_ss.items()}}
+        log(f"steady state: step {ms_ss:.3f} ms, useful {useful / (ms_ss * 1e-3) / 1e12:.1f} TFLOP/s")
+
     if not args.no_baselines:  # (profiled runs time only the step's own launches of each kernel)
         extra["lse_delta_pass"] = delta_pass(A, torch, r, ps, w)
         log(f"lse / delta pass: {json.dumps(extra['lse_delta_pass'])}")

@@ -340,10 +340,10 @@ __device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D
                                           int qlim, int lane) {
   using C = BwdCfg<D>;
   // Hand-scheduled: the S / dP MFMAs (A = Q / dO rows from LDS, B = the K
-  // operands in registers / V rows from LDS), the vector work of query rows 0-15 of the 32 (registers 0-7),
-  // then the dV / dK MFMAs of those rows with the vector work of rows 16-31
-  // between them, then the dV / dK MFMAs of rows 16-31.  Operand reads run
-  // two MFMAs ahead.
+  // operands in registers / V rows from LDS), the vector work of query rows
+  // 0-15 of the 32 (registers 0-7), then the dV / dK MFMAs of those rows
+  // with the vector work of rows 16-31 between them, then the dV / dK MFMAs
+  // of rows 16-31.  Operand reads run two MFMAs ahead.
   constexpr int NSD = 2 * C::NS, NG = 2 * C::NE, N = NSD + 2 * NG;
   const int l32 = lane & 31, hi = lane >> 5;
   struct Ops {
