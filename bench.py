@@ -308,11 +308,12 @@ def skip_cost(A, torch, steps, warmup, copy_gbps):
 def delta_pass(A, torch, r, ps, w, n=20):
     """The row statistics of the backward ("LSE pass"): the forward writes
     LSE (4 bytes per valid row and q head); the dQ kernel's prologue reads O
-    and dO (2 * 2 * D bytes per valid row and q head) and writes Delta =
-    rowsum(dO * O) and LSE * log2(e) (8 bytes).  It is fused into that
-    prologue, so it is timed as the dQ kernel on a copy of the map whose
-    query tiles visit only their first key tile: the prologue (Q, dO, O
-    loads, Delta and LSE2 stores), one tile, and the dQ block.  GB/s =
+    and dO (2 * 2 * D bytes per valid row and q head) and writes -Delta =
+    -rowsum(dO * O) and -LSE / scale (8 bytes; the dK/dV kernel's
+    accumulators start from them).  It is fused into that prologue, so it
+    is timed as the dQ kernel on a copy of the map whose query tiles visit
+    only their first key tile: the prologue (Q, dO, O loads, the two row
+    stores), one tile, and the dQ block.  GB/s =
     algorithmic bytes of the pass / that time, a lower bound on the pass's
     own rate (the run also holds one tile's work, Q's loads and dQ's
     stores; all-pad tiles, which read nothing, are included as in the
@@ -338,7 +339,7 @@ def delta_pass(A, torch, r, ps, w, n=20):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
     t_valid = ps.real_tokens()
-    alg = (2 * 2 * w.D + 8) * w.Hq * t_valid          # O, dO read; Delta, LSE2 written
+    alg = (2 * 2 * w.D + 8) * w.Hq * t_valid          # O, dO read; -Delta, -LSE/scale written
     del m, dq
     return {"fwd_lse_write_bytes": 4 * w.Hq * t_valid, "algorithmic_bytes": alg, "prologue_one_tile_ms": ms,
             "GBps_lower_bound": alg / (ms * 1e-3) / 1e9, "frac_of_hbm_peak": alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,

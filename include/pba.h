@@ -327,9 +327,9 @@ PBA_API int pba_packed_attn_fwd_rope(const pba_block_map* map, const void* q, co
                                      void* o, float* lse, void* q_rot, int B, int S, int Hq, int Hkv, int D,
                                      float softmax_scale, float rope_base, void* stream);
 
-/* Workspace bytes the backward needs: two fp32 [B, Hq, S] arrays (the row
- * dot products rowsum(dO * O) and the log2-domain LSE), written by the dQ
- * stage and read by the dK / dV stage, then the area of the dK / dV stage's
+/* Workspace bytes the backward needs: two fp32 [B, Hq, S] arrays (minus the
+ * row dot products rowsum(dO * O), and minus LSE / softmax_scale), written
+ * by the dQ stage and read by the dK / dV stage, then the area of the dK / dV stage's
  * split key tiles (a key tile whose visit list is longer than the average
  * load of one workgroup slot is shared by two workgroups): arrival counters
  * and fp32 partial sums for at most min(256, B * ceil(S / 128) * Hq)
@@ -357,7 +357,7 @@ PBA_API int pba_packed_attn_bwd(const pba_block_map* qmap, const pba_block_map* 
 /* The backward in its two stages, for callers that schedule or time them
  * separately.  `stages` is a bit mask; running both in order on one stream
  * is exactly pba_packed_attn_bwd:
- *   PBA_BWD_DQ    dQ written; workspace <- rowsum(dO * O) and LSE * log2(e)
+ *   PBA_BWD_DQ    dQ written; workspace <- -rowsum(dO * O) and -LSE / scale
  *   PBA_BWD_DKDV  dK, dV written (reads the workspace the dQ stage wrote)
  * Arguments as for pba_packed_attn_bwd (all are checked for every stage);
  * returns PBA_ERR_SHAPE for an empty or unknown mask. */
