@@ -195,9 +195,9 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   const bf16* vb = a.v + ((int64_t)b * S * Hkv + g) * D;
   const Stager<D, C::STR> kst(tid, kvstride);  // K and V tiles have the same shape
 
-  // Prologue in two rounds, as the Q and dO blocks and the first K/V tile do
-  // not fit in LDS at once: Q and dO into the two buffer pairs (with O into
-  // registers), then the first K/V tile.
+  // Prologue in two load passes, as the Q and dO blocks and the first K/V
+  // tile do not fit in LDS at once: Q and dO into the two buffer pairs (with
+  // O into registers), then the first K/V tile.
   char* const pair0 = (char*)lds;             // K(0) V(0)
   char* const pair1 = (char*)(lds + 2 * T);   // K(1) V(1)
   const int qrows = min(R, S - q0), qrow_bytes = Hq * D * 2;
@@ -208,14 +208,14 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   // Q^T and dO^T as B operands: lane holds query qi, head dims 16*st + 8*hi + 0..7.
   bf16x8 qop[C::NS], dop[C::NS];
   float delta = 0.f;
-  // A query tile that visits no key tile holds only pad rows, whose dQ,
-  // Delta and LSE2 are all 0: its row blocks are not read at all.
+  // A query tile that visits no key tile holds only pad rows, whose dQ and
+  // row values for bwd_dkdv are all 0: its row blocks are not read at all.
   if (n > 0) {
-    // Round 1: the Q and dO blocks into the two buffer pairs (whole-row
-    // direct loads) and, at the same time, this lane's O chunks straight into
-    // registers, in the lane layout of the dO operand (query row qi, head dims
-    // 16*st + 8*hi + 0..7): O is needed only for Delta.  Rows past S read as
-    // zeros through the resource's range.
+    // First load pass: the Q and dO blocks into the two buffer pairs
+    // (whole-row direct loads) and, at the same time, this lane's O chunks
+    // straight into registers, in the lane layout of the dO operand (query
+    // row qi, head dims 16*st + 8*hi + 0..7): O is needed only for Delta.
+    // Rows past S read as zeros through the resource's range.
     Blk::template load<4>(pair1, a.q + blk, qrows, qrow_bytes, w, lane);
     Blk::template load<4>(pair0, a.dout + blk, qrows, qrow_bytes, w, lane);
     u32x4 ov[C::NS];
@@ -245,8 +245,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
     }
     delta += wave_half_swap(delta);
     __syncthreads();
-    // Round 2: the first K/V tile (shared with other query tiles, so mostly
-    // a cache hit).
+    // Second load pass: the first K/V tile (shared with other query tiles,
+    // so mostly a cache hit).
     const int k0 = min(max(first, 0), mp.nkt - 1) * 64;
     kst.stage(sK(0), kb + (int64_t)k0 * kvstride, S - k0);
     kst.stage(sV(0), vb + (int64_t)k0 * kvstride, S - k0);
@@ -327,10 +327,10 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
 // tile).  Query q0 + 8*(r/4) + 4*hi + r%4 sits in register r of s.  The
 // score and dP accumulators start from -LSE / scale and -Delta (staged
 // per row in s0 and dp0), so they finish as S - LSE / scale, whose
-// exp2(scale_log2 * x) is P, and dP - Delta: no per-score subtraction.  On partial tiles
-// (MASK) the lane's key kj is seen by queries [kj, qend): row index x of the
-// tile is visible iff (unsigned)(x - qrel) < (unsigned)qlim (qrel = kj - the
-// tile's first query, qlim = qend - kj).  These compares depend on the tile
+// exp2(scale_log2 * x) is P, and dP - Delta: no per-score subtraction.  On
+// partial tiles (MASK) the lane's key kj is seen by queries [kj, qend): row
+// index x of the tile is visible iff (unsigned)(x - qrel) < (unsigned)qlim
+// (qrel = kj - the tile's first query, qlim = qend - kj).  These compares depend on the tile
 // only, so the compiler keeps them in scalar lane masks across the q heads.
 template <int D, bool MASK>
 __device__ __forceinline__ void dkdv_step(f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D / 32], const bf16x8 (&kop)[D / 16],
@@ -503,8 +503,8 @@ __device__ __forceinline__ void part_add(f32x16 (&acc)[D / 32], const float* p, 
 // K and V of the 128 keys are staged once: each wave reads its 32 keys' K
 // operands (B operands of S) into registers, while V stays in LDS (B
 // operands of dP, read per step); Q, dO and the 64 rows' -LSE / scale and
-// -Delta are staged by direct loads into a double buffer.  The two waves that share keys sum their partial dK / dV
-// through LDS at the end.
+// -Delta are staged by direct loads into a double buffer.  The two waves
+// that share keys sum their partial dK / dV through LDS at the end.
 template <int D>
 __global__ void __launch_bounds__(512, 1) bwd_dkdv(BwdArgs a) {
   using C = BwdCfg<D>;

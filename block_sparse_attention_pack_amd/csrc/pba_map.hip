@@ -271,10 +271,10 @@ __device__ void map_totals(const MapOut& m, int B, int64_t* s_red) {
 // visible pairs row by row.  For a k2q list the key runs of the column's
 // keys (key j is seen by the queries [j, q_end)) reduce to a prefix maximum
 // and a minimum of the run ends, which decide each query tile in O(1).  Both
-// sides decide from the exact visible pairs, so both agree.  The full tiles are written in ascending order by ballot
-// compaction, then the partial ones (classes recomputed for lists of more
-// than 64 tiles), then -1 fill and the counts; q2k waves also write the
-// classes.  The last block to finish a group (all lists of one side of one
+// sides decide from the exact visible pairs, so both agree.  The full
+// tiles are written in ascending order by ballot compaction, then the
+// partial ones (classes recomputed for lists of more than 64 tiles), then -1
+// fill and the counts; q2k waves also write the classes.  The last block to finish a group (all lists of one side of one
 // map) sorts that side's work order and, for the query side, sums the map's
 // totals; sides of more than kOrderLds tiles are left to map_order.
 __global__ void __launch_bounds__(kTilesThreads) map_tiles(MapSet ms) {
