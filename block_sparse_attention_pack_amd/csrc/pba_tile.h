@@ -250,7 +250,12 @@ struct RowBlock {
     }
 #endif
   }
-  // LDS -> HBM by NT threads, rows >= rows_valid skipped.
+  // LDS -> HBM by NT threads, rows >= rows_valid skipped.  The stores are
+  // non-temporal: every caller stores an output block that its kernel does
+  // not read again, and keeping those lines out of the caches leaves them to
+  // the tiles that are re-read (whole step 564 -> 537 us at the
+  // Qwen3-8B-shaped packs, even though the dQ kernel then reads O from
+  // memory).
   template <int NT>
   __device__ __forceinline__ static void store(void* g, const char* lds, int rows_valid, int row_bytes, int tid) {
     constexpr int RC = RB / 16, TOTAL = R * RC;
@@ -259,7 +264,8 @@ struct RowBlock {
       const int c = tid + NT * i;
       const int p = c / RC, cc = c % RC;
       if ((TOTAL % NT == 0 || c < TOTAL) && p < rows_valid)
-        *(u32x4*)((char*)g + (int64_t)p * row_bytes + 16 * cc) = *(const u32x4*)(lds + p * LSTR + 16 * cc);
+        __builtin_nontemporal_store(*(const u32x4*)(lds + p * LSTR + 16 * cc),
+                                    (u32x4*)((char*)g + (int64_t)p * row_bytes + 16 * cc));
     }
   }
 };
