@@ -126,6 +126,64 @@ __device__ __forceinline__ void dq_tile(f32x16 (&dq)[D / 32], const bf16x8 (&qop
   });
 }
 
+// dq_tile for one 32-key half aa of a partial tile whose other half no
+// query of the wave sees (its dS, hence its dQ term, is exactly zero): S^T
+// and dP^T of the half, its dS^T (kmw: the half's word of the key mask),
+// then its dQ^T MFMAs.
+template <int D, bool MASK>
+__device__ __forceinline__ void dq_half(f32x16 (&dq)[D / 32], const bf16x8 (&qop)[D / 16],
+                                        const bf16x8 (&dop)[D / 16], float l2, float delta,
+                                        const bf16* __restrict__ sk, const bf16* __restrict__ sv, float scale_log2,
+                                        unsigned kmw, int aa, int lane) {
+  using C = BwdCfg<D>;
+  constexpr int NSD = 2 * C::NS;  // S and dP MFMAs
+  constexpr int NDQ = 2 * C::NE;  // dQ MFMAs
+  constexpr int N = NSD + NDQ;
+  const int l32 = lane & 31, hi = lane >> 5;
+  // prow keeps 32-row blocks in place, so the half's rows start 32*aa rows in.
+  const bf16* skh = sk + 32 * aa * C::STR;
+  const bf16* svh = sv + 32 * aa * C::STR;
+  auto operand = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+    if (i < NSD) {  // S (even) / dP (odd), k-step i / 2
+      const int st = i >> 1;
+      return *(const bf16x8*)(((i & 1) ? svh : skh) + prow(l32) * C::STR + 16 * st + 8 * hi);
+    }
+    const int k = i - NSD, e = k >> 1, u = k & 1;
+    const int r0 = 16 * u + 4 * hi;
+    return lds_tr8p(skh, C::STR, r0, r0 + 8, 32 * e, lane);
+  };
+  f32x16 s = f32x16{}, dp = f32x16{};
+  bf16x8 ds[2];
+  bf16x8 ops[3];
+  ops[0] = operand(0);
+  ops[1] = operand(1);
+  sched_fence();
+  static_for<0, N>([&](auto ic) __attribute__((always_inline)) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i + 2 < N) ops[(i + 2) % 3] = operand(i + 2);
+    if constexpr (i < NSD) {
+      constexpr int st = i >> 1;
+      if constexpr (i & 1) dp = mfma32(ops[i % 3], dop[st], dp);
+      else s = mfma32(ops[i % 3], qop[st], s);
+      if constexpr (i == NSD - 1) {
+        sched_fence();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -l2));
+          if (MASK) p = keep_or_zero(mask_bit(kmw, 8 * (r >> 2) + (r & 3)), p);
+          s[r] = p * (dp[r] - delta);
+        }
+        ds[0] = pack8(s, 0);
+        ds[1] = pack8(s, 8);
+      }
+    } else {
+      constexpr int k = i - NSD, e = k >> 1, u = k & 1;
+      dq[e] = mfma32(ops[i % 3], ds[u], dq[e]);
+    }
+    sched_fence();
+  });
+}
+
 template <int D, int WGH>
 __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
   using C = BwdCfg<D>;
@@ -275,8 +333,22 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
     }
     if constexpr (decltype(masked)::value) {
       const int jb = kt * 64 + 4 * hi;
-      dq_tile<D, true>(dq, qop, dop, l2, delta, sK(buf), sV(buf), a.scale_log2,
-                       key_mask(qi - jb, wlo - jb, jb - wplo, wphi - wplo), lane);
+      const KeyMask km = key_mask(qi - jb, wlo - jb, jb - wplo, wphi - wplo);
+      // Which 32-key halves some query of the wave sees (the bits of a
+      // lane's 16 scores in each mask word are 0x0F0F0F0F).  A half no
+      // query sees adds exactly zero, so only the other is computed (with
+      // 4 q heads per workgroup, 5% of the MFMA work at Qwen3-8B-shaped
+      // packs: the diagonal tiles whose second half lies after every query
+      // of the block).  When neither half is seen (possible with fewer heads
+      // per workgroup, whose waves cover different queries), the one-half
+      // body runs with an all-zero mask and adds zero.
+      const bool see0 = __builtin_amdgcn_ballot_w64((km.lo & 0x0F0F0F0Fu) != 0) != 0;
+      const bool see1 = __builtin_amdgcn_ballot_w64((km.hi & 0x0F0F0F0Fu) != 0) != 0;
+      if (see0 && see1)
+        dq_tile<D, true>(dq, qop, dop, l2, delta, sK(buf), sV(buf), a.scale_log2, km, lane);
+      else
+        dq_half<D, true>(dq, qop, dop, l2, delta, sK(buf), sV(buf), a.scale_log2, see0 ? km.lo : km.hi, see0 ? 0 : 1,
+                         lane);
     } else {
       dq_tile<D, false>(dq, qop, dop, l2, delta, sK(buf), sV(buf), a.scale_log2, KeyMask{0u, 0u}, lane);
     }
