@@ -16,6 +16,7 @@ from workloads.generate import Pack, PackSet, descriptor_arrays, make_workload, 
 pytestmark = pytest.mark.gpu
 
 O_ABS, O_REL, LSE_ABS, G_REL = 1e-2, 1e-2, 1e-3, 1e-2
+G_ABS_ZERO = 1e-3  # gradients whose exact value is 0 (fp32 cancellation only)
 
 
 def _mask(ps):
@@ -36,13 +37,19 @@ def _check_full(w, got, tag):
     assert rel_l2(o[valid], O[valid]) <= O_REL, (tag, rel_l2(o[valid], O[valid]))
     lse = got["lse"].to(torch.float64)
     vl = valid[:, None, :].expand_as(lse)
-    assert float((lse[vl] - L[vl]).abs().max()) <= LSE_ABS, tag
+    if bool(vl.any()):
+        assert float((lse[vl] - L[vl]).abs().max()) <= LSE_ABS, tag
     assert torch.isneginf(lse[~vl]).all(), tag
     assert (o[~valid] == 0).all(), tag
     for name, x, ref in (("dq", got["dq"], dq), ("dk", got["dk"], dk), ("dv", got["dv"], dv)):
         x = x.to(torch.float64)
-        e = rel_l2(x[valid], ref[valid])
-        assert e <= G_REL, (tag, name, e)
+        if float(ref[valid].norm()) > 0:
+            e = rel_l2(x[valid], ref[valid])
+            assert e <= G_REL, (tag, name, e)
+        elif bool(valid.any()):
+            # Every query sees one key only (P = 1, so dS = dP - rowsum(dO * O)
+            # = 0 exactly): only the fp32 rounding of that difference remains.
+            assert float(x[valid].abs().max()) <= G_ABS_ZERO, (tag, name)
         assert (x[~valid] == 0).all(), (tag, name)
     return True
 
@@ -85,6 +92,30 @@ def test_unscaled_multi_tile(heads):
     w = make_workload(None, 3, packset=ps, heads=heads)
     say("parity unscaled multi-tile", heads)
     _check_full(w, run_fwd_bwd(w), f"multi {heads}")
+
+
+# Degenerate layouts: a one-token row; a row of pad only; a pack with an
+# empty prompt and two empty branches beside an all-pad row; an empty first
+# response (its sibling then forms one run with the prompt); a prompt-only
+# pack, an empty pack and 40 one-token responses; rows that end inside the
+# first tile, one of them holding a single token at its last position.
+EDGE_LAYOUTS = [
+    PackSet(1, 1, [Pack(0, 0, 1, ())]),
+    PackSet(1, 5, []),
+    PackSet(2, 70, [Pack(1, 0, 0, (0, 0, 70))]),
+    PackSet(1, 130, [Pack(0, 0, 64, (0, 66))]),
+    PackSet(1, 200, [Pack(0, 3, 5, ()), Pack(0, 8, 0, ()), Pack(0, 8, 0, (1,) * 40)]),
+    PackSet(2, 17, [Pack(0, 0, 3, (7, 7)), Pack(1, 16, 1, ())]),
+]
+
+
+@pytest.mark.parametrize("heads", [(4, 2, 128), (8, 2, 64), (3, 1, 64)])
+@pytest.mark.parametrize("case", range(len(EDGE_LAYOUTS)))
+def test_edge_layouts(case, heads):
+    ps = EDGE_LAYOUTS[case]
+    w = make_workload(None, 5, packset=ps, heads=heads)
+    say("parity edge", case, heads, ps.B, ps.S, len(ps.packs))
+    _check_full(w, run_fwd_bwd(w), f"edge {case} {heads}")
 
 
 def test_pad_inertness():

@@ -11,7 +11,7 @@ import torch
 import oracle
 from oracle import rope as R
 from gpu_path import api, build_map, say
-from workloads.generate import descriptor_arrays, make_packset, random_packset
+from workloads.generate import Pack, PackSet, descriptor_arrays, make_packset, random_packset
 
 pytestmark = pytest.mark.gpu
 
@@ -222,14 +222,37 @@ def test_fused_rope_variants_vs_oracle(heads):
     heads per workgroup 4, 2 and 1 at D = 64 and 128) against the oracle on
     random ragged packs: O on rotated inputs, dQ and dK rotated back to the
     unrotated Q and K, dV; whole tensors, every valid element."""
-    from workloads.generate import make_workload
     rng = np.random.default_rng(4200 + 7 * heads[0] + heads[2])
     ps = random_packset(rng, B=2, S=int(rng.integers(150, 400)), max_packs_per_row=3, max_resp=3, max_len=110)
     if not ps.packs:
         ps = make_packset(1)
+    say("fused rope variant", heads, ps.B, ps.S, len(ps.packs))
+    _rope_vs_oracle(ps, heads)
+
+
+# Short and degenerate layouts: a pack with an empty prompt and two empty
+# branches beside an all-pad row; an empty first response; a prompt-only
+# pack, an empty pack and 40 one-token responses; rows ending inside the
+# first tile, one holding a single token at its last position.
+ROPE_EDGE_LAYOUTS = [
+    PackSet(2, 70, [Pack(1, 0, 0, (0, 0, 70))]),
+    PackSet(1, 130, [Pack(0, 0, 64, (0, 66))]),
+    PackSet(1, 200, [Pack(0, 3, 5, ()), Pack(0, 8, 0, ()), Pack(0, 8, 0, (1,) * 40)]),
+    PackSet(2, 17, [Pack(0, 0, 3, (7, 7)), Pack(1, 16, 1, ())]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(ROPE_EDGE_LAYOUTS)))
+def test_fused_rope_edge_layouts(case):
+    ps = ROPE_EDGE_LAYOUTS[case]
+    say("fused rope edge", case, ps.B, ps.S, len(ps.packs))
+    _rope_vs_oracle(ps, (4, 2, 128))
+
+
+def _rope_vs_oracle(ps, heads):
+    from workloads.generate import make_workload
     w = make_workload(None, 6, packset=ps, heads=heads, unscaled=True)
     base = 1e4
-    say("fused rope variant", heads, ps.B, ps.S, len(ps.packs))
     got = _rope_case(w, base)
     pk, br, _ = oracle.token_ids(got["P"], got["R"], ps.B, ps.S)
     mask = oracle.attention_mask(pk, br)
