@@ -6,7 +6,9 @@ DPO loss -log sigmoid(u_+ - u_-) (a closed form); hand-evaluated values at
 u = 0 tell the four forms apart; the coefficients equal central finite
 differences of L_group; each group's gradient sums to zero (every form
 depends on differences of u only); a response shared by two groups gets
-the sum of both groups' terms; the NLL weights have a closed form.
+the sum of both groups' terms; the NLL weights have a closed form; the
+forms agree with one another where their definitions meet (one positive,
+members with equal rewards) and none depends on the order of members.
 """
 import math
 
@@ -128,3 +130,33 @@ def test_validation():
     assert gd.validate_groups([([0], [1]), ([2], [2])], 4) == 1     # positive and negative
     assert gd.validate_groups([([0, 0], [1])], 4) == 0              # duplicate
     assert gd.validate_groups([([0], [4])], 4) == 0                 # out of range
+
+
+def test_forms_agree_where_their_definitions_meet():
+    """Cross-checks between the forms (each computed by its own branch of
+    the oracle): with one positive, MPO and the softmax form are both the
+    negative log-probability of the positive under a softmax over the group;
+    when all positives share one reward and all negatives another, all-pairs
+    and margin reduce to the one-pair DPO loss and the softmax form to the
+    one-positive case; none depends on the order of members; all tend to 0
+    as the negatives' rewards fall."""
+    rng = np.random.default_rng(17)
+    for k in range(1, 6):
+        up = float(rng.normal())
+        un = rng.normal(size=k)
+        z = np.concatenate([[up], un])
+        want = float(np.log(np.exp(z - z.max()).sum()) + z.max() - up)
+        assert abs(gd.phi("mpo", [up], un) - want) < 1e-13
+        assert abs(gd.phi("softmax", [up], un) - want) < 1e-13
+    for nP in (1, 2, 4):
+        for nN in (1, 3):
+            a, b = float(rng.normal()), float(rng.normal())
+            for obj in ("all_pairs", "margin"):
+                assert abs(gd.phi(obj, [a] * nP, [b] * nN) - _dpo(a - b)) < 1e-13, obj
+            one = gd.phi("softmax", [a], [b] * nN)
+            assert abs(gd.phi("softmax", [a] * nP, [b] * nN) - one) < 1e-13
+    for obj in gd.OBJECTIVES:
+        uP, uN = rng.normal(size=3), rng.normal(size=4)
+        base = gd.phi(obj, uP, uN)
+        assert abs(gd.phi(obj, uP[::-1], rng.permutation(uN)) - base) < 1e-13, obj
+        assert 0.0 <= gd.phi(obj, uP, uN - 60.0) < 1e-20, obj
