@@ -33,7 +33,7 @@ from .segments import (  # noqa: F401
     STATUS, token_ids, attention_mask, attention_mask_rows, token_windows, block_map, allowed_count,
 )
 from .attention import (  # noqa: F401
-    attn_fwd, attn_bwd, attn_fwd_rows, attn_dq_rows, attn_bwd_sampled, useful_flops,
+    attn_fwd, attn_bwd, attn_fwd_rows, attn_dq_rows, attn_dkdv_rows, attn_bwd_sampled, useful_flops,
 )
 from .positions import positions  # noqa: F401
 from .logprob import row_logsumexp, token_logp, response_logp  # noqa: F401

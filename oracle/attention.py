@@ -120,6 +120,35 @@ def attn_dq_rows(q, k, v, do, mask_rows, b, h, qrows, scale):
     return scale * (dS @ k[b, :, g])
 
 
+def attn_dkdv_rows(q, k, v, do, mask_rows, b, g, qrows, krows, scale):
+    """dK [m, D] and dV [m, D] of the listed key rows of (batch row b, kv
+    group g) for the loss <dO, O>, summed over the group's q heads.
+    mask_rows [n, S] are the mask rows of the query rows qrows, which must
+    hold every query that sees a listed key (no other query contributes to
+    those keys).  Each query's softmax comes from its own full row: P_i,
+    O_i = P_i V, Delta_i = dO_i . O_i; for a listed key j,
+    dS_ij = P_ij (dO_i . V_j - Delta_i), dV_j = sum_i P_ij dO_i and
+    dK_j = scale sum_i dS_ij Q_i (so that very long rows need no S x S
+    mask)."""
+    q, k, v, do = _t(q), _t(k), _t(v), _t(do)
+    G = q.shape[2] // k.shape[2]
+    qi = torch.as_tensor(np.asarray(qrows), dtype=torch.long)
+    kj = torch.as_tensor(np.asarray(krows), dtype=torch.long)
+    m = torch.from_numpy(np.ascontiguousarray(mask_rows))
+    kg, vg = k[b, :, g], v[b, :, g]
+    dk = torch.zeros((len(kj), k.shape[3]), dtype=torch.float64)
+    dv = torch.zeros_like(dk)
+    for h in range(g * G, (g + 1) * G):
+        P, _ = _probs(q[b, qi, h], kg, m, scale)
+        dOi = do[b, qi, h]
+        delta = (dOi * (P @ vg)).sum(dim=1)
+        Pj = P[:, kj]
+        dS = Pj * (dOi @ vg[kj].T - delta[:, None])
+        dv += Pj.T @ dOi
+        dk += scale * (dS.T @ q[b, qi, h])
+    return dk, dv
+
+
 def attn_bwd_sampled(q, k, v, do, mask_b, b, g, qrows, krows, scale):
     """Gradients at sampled positions of batch row b and kv group g:
     dQ[qrows] for every q head of the group ([G, n, D]) and dK[krows],

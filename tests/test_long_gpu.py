@@ -7,12 +7,15 @@ Checked against the oracle where it can compute one row at a time
 (forward rows, dQ rows: each needs only that row's keys), and through
 properties that hold at any size for dK and dV (with P's rows summing to 1:
 sum_j dV_j = sum_i dO_i over each kv group's q heads, and sum_j dK_j = 0
-because each row of dS sums to 0).  Tolerances: O and LSE as for the
-workloads on every checked row; dQ rel-L2 1e-2 over uniformly drawn rows
+because each row of dS sums to 0), and row by row for the keys among each
+response's last 1024 tokens, which only those tokens' queries see.
+Tolerances: O and LSE as for the workloads on every checked row; dQ
+rel-L2 1e-2 over uniformly drawn rows
 (an estimate of the whole tensor's), and per row 2e-2 on the boundary rows
 (rows that see only two or three keys carry the largest relative error:
 their dS is a difference of two nearly equal terms, Delta coming from the
-bf16 O); the dV sum to rel 1e-2; the dK sum must be far below the
+bf16 O); dK and dV rows at the branch ends rel-L2 1e-2 over the checked keys
+and 3e-2 per key; the dV sum to rel 1e-2; the dK sum must be far below the
 root-sum-square of the dK rows (a sum of 131 072 independently rounded terms
 lands near 2^-9 of it; 0.05 leaves 25x margin, while a missing or
 mis-scaled term lands near 1)."""
@@ -90,6 +93,28 @@ def test_one_pack_of_131072_tokens():
         assert bool((err <= 2e-2 * dQ[:ne].norm(dim=1) + 1e-6).all()), (h, err.tolist())
 
     G = Hq // Hkv
+    # dK / dV rows at the end of each response: a key among a branch's last
+    # 1024 tokens is seen only by that branch's queries from the key on, so
+    # those 1024 query rows give the oracle's exact values (each query's
+    # softmax still runs over all of its ~65 000-98 000 keys).
+    gk = 5
+    ks, vs = k[:, :, gk:gk + 1].cpu(), v[:, :, gk:gk + 1].cpu()
+    for end in (p + r1, S):
+        qrows = np.arange(end - 1024, end)
+        keys = np.unique(np.concatenate([[end - 1024, end - 1023, end - 513, end - 2, end - 1],
+                                         np.random.default_rng(end).choice(qrows, size=11, replace=False)]))
+        mr = oracle.attention_mask_rows(pk, br, 0, qrows)
+        qs = q[:, qrows, gk * G:(gk + 1) * G].cpu()
+        dos = do[:, qrows, gk * G:(gk + 1) * G].cpu()
+        dK, dV = oracle.attn_dkdv_rows(qs, ks, vs, dos, mr, 0, 0, np.arange(len(qrows)), keys, scale)
+        for name, got, ref in (("dk", dk, dK), ("dv", dv, dV)):
+            x = got[0, keys, gk].cpu().double()
+            e = _rel(x, ref)
+            say("  branch end", end, name, "rel-L2 on", len(keys), "key rows", e)
+            assert e <= 1e-2, (end, name, e)
+            err = (x - ref).norm(dim=1)
+            assert bool((err <= 3e-2 * ref.norm(dim=1) + 1e-6).all()), (end, name, err.tolist())
+
     for gk in range(Hkv):
         sum_dv = dv[0, :, gk].float().sum(0).double().cpu()
         sum_do = do[0, :, gk * G:(gk + 1) * G].float().sum((0, 1)).double().cpu()

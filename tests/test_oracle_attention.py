@@ -290,3 +290,40 @@ def test_dq_rows_by_finite_differences():
             qm[0, i, h, d] -= eps
             num = (_loss(qp, k, v, do, m, scale) - _loss(qm, k, v, do, m, scale)) / (2 * eps)
             assert abs(num - float(dq_rows[n, d])) <= 1e-7 * max(1.0, abs(num))
+
+
+def test_dkdv_rows_by_finite_differences():
+    """attn_dkdv_rows is the gradient of <dO, O> with respect to the listed
+    key rows (central differences on K and V, which every q head of the
+    group shares), it equals the full backward's rows, and the query rows
+    that see the listed keys are all it needs: at keys in the last tokens of
+    a branch, the rows from the first listed key to the branch's end give
+    the same values."""
+    pl = [(0, 0, 4, (3, 5)), (0, 12, 2, (2,)), (0, 17, 0, (3,))]
+    S, Hq, Hkv, D, scale = 22, 4, 2, 8, 0.37
+    m = _mask(1, S, pl)
+    q, k, v, do = _rand((1, S, Hq, D), 71), _rand((1, S, Hkv, D), 72), _rand((1, S, Hkv, D), 73), _rand((1, S, Hq, D), 74)
+    _, dk, dv = oracle.attn_bwd(q, k, v, do, m, scale)
+    every = list(range(S))
+    keys = [0, 3, 4, 6, 9, 11, 12, 15, 18, 21]
+    g = 1
+    dk_rows, dv_rows = oracle.attn_dkdv_rows(q, k, v, do, m[0], 0, g, every, keys, scale)
+    assert torch.allclose(dk_rows, dk[0, keys, g], atol=1e-13, rtol=0)
+    assert torch.allclose(dv_rows, dv[0, keys, g], atol=1e-13, rtol=0)
+    # the second response of the first pack is tokens 7..11: keys 9..11 are
+    # seen by queries 9..11 only
+    tail, qs = [9, 10, 11], [9, 10, 11]
+    dk_t, dv_t = oracle.attn_dkdv_rows(q, k, v, do, m[0][qs], 0, g, qs, tail, scale)
+    assert torch.allclose(dk_t, dk[0, tail, g], atol=1e-13, rtol=0)
+    assert torch.allclose(dv_t, dv[0, tail, g], atol=1e-13, rtol=0)
+    eps = 1e-6
+    for n, j in enumerate(keys):
+        for d in (0, 5):
+            for x, got in ((k, dk_rows), (v, dv_rows)):
+                xp, xm = x.clone(), x.clone()
+                xp[0, j, g, d] += eps
+                xm[0, j, g, d] -= eps
+                args_p = (q, xp, v) if x is k else (q, k, xp)
+                args_m = (q, xm, v) if x is k else (q, k, xm)
+                num = (_loss(*args_p, do, m, scale) - _loss(*args_m, do, m, scale)) / (2 * eps)
+                assert abs(num - float(got[n, d])) <= 1e-7 * max(1.0, abs(num))
