@@ -1,7 +1,9 @@
 """HIP forward / backward vs the fp64 oracle.
 
-Acceptance: O max-abs <= 1e-2 and rel-L2 <= 1e-2; LSE abs <= 1e-3 on valid
-rows; dQ, dK, dV rel-L2 <= 1e-2; pad rows O = 0, LSE = -inf, zero grads.
+Acceptance: O max-abs <= 1e-2 (plus the bf16 rounding of O and of P, which
+matters only for unscaled inputs) and rel-L2 <= 1e-2; LSE abs <= 1e-3 on
+valid rows; dQ, dK, dV rel-L2 <= 1e-2; pad rows O = 0, LSE = -inf, zero
+grads.
 """
 import math
 
@@ -33,7 +35,15 @@ def _check_full(w, got, tag):
     valid = torch.from_numpy(pk >= 0)                      # [B, S]
     vq = valid[:, :, None, None]
     o = got["o"].to(torch.float64)
-    assert float((o - O).abs().max()) <= O_ABS, tag
+    # Element bound: O_ABS plus what bf16 rounding alone allows, 2^-8 of
+    # |O| for the rounded output and 2^-8 of sum_j P_ij |V_j| for the
+    # rounded P operand (the oracle's attention of |V|).  With inputs scaled
+    # by 1/sqrt(128) that adds about 1e-3; with unscaled N(0, 1) inputs |O|
+    # reaches 4, where bf16's spacing is 2^-5 and O_ABS alone cannot hold.
+    absv, _ = oracle.attn_fwd(w.q, w.k, w.v.abs(), m, w.scale)
+    bound = O_ABS + 2.0 ** -8 * (O.abs() + absv)
+    worst = float(((o - O).abs() - bound).max())
+    assert worst <= 0, (tag, worst)
     assert rel_l2(o[valid], O[valid]) <= O_REL, (tag, rel_l2(o[valid], O[valid]))
     lse = got["lse"].to(torch.float64)
     vl = valid[:, None, :].expand_as(lse)
@@ -116,6 +126,25 @@ def test_edge_layouts(case, heads):
     w = make_workload(None, 5, packset=ps, heads=heads)
     say("parity edge", case, heads, ps.B, ps.S, len(ps.packs))
     _check_full(w, run_fwd_bwd(w), f"edge {case} {heads}")
+
+
+SWEEP_HEADS = [(8, 2, 64), (4, 2, 128), (3, 1, 64), (8, 2, 128)]
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_layout_sweep(seed):
+    """Many small random layouts (1 to 3 rows, 1 to 640 tokens, empty rows,
+    zero-length prompts and branches, gaps), each variant family in turn:
+    lengths that end anywhere inside a tile, whole tensors against the
+    oracle."""
+    rng = np.random.default_rng(7000 + seed)
+    B, S = int(rng.integers(1, 4)), int(rng.integers(1, 641))
+    ps = random_packset(rng, B=B, S=S, max_packs_per_row=int(rng.integers(1, 5)), max_resp=4,
+                        max_len=int(rng.integers(1, max(2, S // 3 + 1))))
+    heads = SWEEP_HEADS[seed % len(SWEEP_HEADS)]
+    w = make_workload(None, seed, packset=ps, heads=heads, unscaled=bool(seed % 3 == 0))
+    say("parity sweep", seed, heads, ps.B, ps.S, len(ps.packs))
+    _check_full(w, run_fwd_bwd(w), f"sweep {seed}")
 
 
 def test_pad_inertness():
