@@ -135,14 +135,14 @@ SWEEP_HEADS = [(8, 2, 64), (4, 2, 128), (3, 1, 64), (8, 2, 128)]
 def test_random_layout_sweep(seed):
     """Many small random layouts (1 to 3 rows, 1 to 640 tokens, empty rows,
     zero-length prompts and branches, gaps), each variant family in turn:
-    lengths that end anywhere inside a tile, whole tensors against the
-    oracle."""
+    lengths that end anywhere inside a tile, N(0, 1) values, whole tensors
+    against the oracle."""
     rng = np.random.default_rng(7000 + seed)
     B, S = int(rng.integers(1, 4)), int(rng.integers(1, 641))
     ps = random_packset(rng, B=B, S=S, max_packs_per_row=int(rng.integers(1, 5)), max_resp=4,
                         max_len=int(rng.integers(1, max(2, S // 3 + 1))))
     heads = SWEEP_HEADS[seed % len(SWEEP_HEADS)]
-    w = make_workload(None, seed, packset=ps, heads=heads, unscaled=bool(seed % 3 == 0))
+    w = make_workload(None, seed, packset=ps, heads=heads)
     say("parity sweep", seed, heads, ps.B, ps.S, len(ps.packs))
     _check_full(w, run_fwd_bwd(w), f"sweep {seed}")
 
