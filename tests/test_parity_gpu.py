@@ -147,6 +147,17 @@ def test_random_layout_sweep(seed):
     _check_full(w, run_fwd_bwd(w), f"sweep {seed}")
 
 
+@pytest.mark.parametrize("heads", [(64, 8, 128), (16, 16, 64), (40, 8, 64)])
+def test_many_heads(heads):
+    """More q heads per workgroup grid (64 q heads over 8 kv heads), one kv
+    head per q head, and G = 5 (one q head per workgroup) on a two-row
+    layout whose lengths end inside tiles."""
+    ps = PackSet(2, 333, [Pack(0, 0, 100, (90, 77)), Pack(0, 270, 20, (13, 30)), Pack(1, 5, 0, (64, 199))])
+    w = make_workload(None, 9, packset=ps, heads=heads)
+    say("parity many heads", heads)
+    _check_full(w, run_fwd_bwd(w), f"heads {heads}")
+
+
 def test_pad_inertness():
     """Changing pad-token values changes no valid output bit."""
     ps = PackSet(1, 300, [Pack(0, 5, 100, (50, 60)), Pack(0, 230, 20, (30,))])
