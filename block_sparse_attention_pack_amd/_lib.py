@@ -295,6 +295,22 @@ def _tensor(x, name: str, shape=None, dtype=torch.bfloat16, device=None, align: 
         raise ValueError(f"{name} must be {align}-byte aligned")
 
 
+def _disjoint(outputs: dict, inputs: dict):
+    """Reject outputs whose memory overlaps an input or another output (the
+    kernels read inputs while other workgroups write outputs)."""
+    def span(t):
+        n = t.numel() * t.element_size()
+        return (t.data_ptr(), t.data_ptr() + n) if n else None
+    outs = [(k, span(t)) for k, t in outputs.items()]
+    ins = [(k, span(t)) for k, t in inputs.items()]
+    for i, (name, a) in enumerate(outs):
+        if a is None:
+            continue
+        for other, b in ins + outs[i + 1:]:
+            if b is not None and a[0] < b[1] and b[0] < a[1]:
+                raise ValueError(f"{name} overlaps {other} in memory")
+
+
 def _bf16(x, name: str, shape=None, device=None):
     _tensor(x, name, shape, torch.bfloat16, device)
 
@@ -349,6 +365,7 @@ def packed_attn_fwd(m: BlockMap, q, k, v, softmax_scale: Optional[float] = None,
         o, lse = out
         _bf16(o, "o", q.shape, q.device)
         _tensor(lse, "lse", (B, Hq, S), torch.float32, q.device, align=4)
+        _disjoint({"o": o, "lse": lse}, {"q": q, "k": k, "v": v})
     _check(_lib.pba_packed_attn_fwd(ctypes.byref(m.struct), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                     lse.data_ptr(), B, S, Hq, Hkv, D, scale, _stream(stream)), "pba_packed_attn_fwd")
     return o, lse
@@ -372,6 +389,8 @@ def _bwd_operands(qmap, kmap, q, k, v, o, lse, dout, out, workspace, qname="q", 
     if workspace is None:
         workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
     ws, ws_bytes = _workspace(workspace, need, q.device)
+    _disjoint({"dq": dq, "dk": dk, "dv": dv, "workspace": workspace},
+              {qname: q, kname: k, "v": v, "o": o, "lse": lse, "dout": dout})
     return (B, S, Hq, Hkv, D), (dq, dk, dv), ws, ws_bytes
 
 
@@ -410,6 +429,7 @@ def packed_attn_bwd_noalloc(qmap: BlockMap, kmap: BlockMap, q, k, v, o, lse, dou
         _bf16(dq, "dq", q.shape, q.device)
         _bf16(dk, "dk", k.shape, q.device)
         _bf16(dv, "dv", k.shape, q.device)
+        _disjoint({"dq": dq, "dk": dk, "dv": dv}, {"q": q, "k": k, "v": v, "o": o, "lse": lse, "dout": dout})
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     _check(_lib.pba_packed_attn_bwd_noalloc(ctypes.byref(qmap.struct), ctypes.byref(kmap.struct), q.data_ptr(),
                                             k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
@@ -453,6 +473,10 @@ def packed_attn_fwd_rope(m: BlockMap, q, k_rot, v, rope_base: float, softmax_sca
     else:
         q_rot = q_rot_out
         _bf16(q_rot, "q_rot_out", q.shape, q.device)
+    outs = {"o": o, "lse": lse}
+    if q_rot is not None:
+        outs["q_rot_out"] = q_rot
+    _disjoint(outs, {"q": q, "k_rot": k_rot, "v": v})
     _check(_lib.pba_packed_attn_fwd_rope(ctypes.byref(m.struct), q.data_ptr(), k_rot.data_ptr(), v.data_ptr(),
                                          o.data_ptr(), lse.data_ptr(), None if q_rot is None else q_rot.data_ptr(),
                                          B, S, Hq, Hkv, D, scale, float(rope_base), _stream(stream)),

@@ -42,6 +42,11 @@
  *   - Layouts (row-major, contiguous): Q, O, dO, dQ [B, S, Hq, D];
  *     K, V, dK, dV [B, S, Hkv, D]; LSE [B, Hq, S].  q head h uses kv head
  *     h / (Hq / Hkv).  Pointers must be 16-byte aligned.
+ *   - Output arrays (and a workspace) must not overlap any input array of
+ *     the same call or each other: the kernels read inputs while other
+ *     workgroups write outputs, so an overlap gives undefined values (it
+ *     cannot make an access leave the arrays).  The library does not check
+ *     this; the Python binding does.
  *   - Supported: D in {64, 128}; Hq % Hkv == 0; bf16 tensors; gfx950.
  *   - Pad tokens (inside a row but in no pack) must hold finite values; they
  *     never influence valid outputs and get O = 0, LSE = -inf and zero

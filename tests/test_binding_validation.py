@@ -1,8 +1,9 @@
 """The Python binding rejects mismatched tensors with ValueError before any
 pointer reaches the library (a wrong shape, dtype or device would otherwise
-become out-of-bounds device accesses).  The first group runs on the CPU
-(host tensors are refused before anything touches a device); the second
-needs device tensors but launches no kernel."""
+become out-of-bounds device accesses), and outputs that overlap an input or
+each other.  The CPU tests need no device (host tensors are refused before
+anything touches one); the gpu-marked ones need device tensors but launch
+no kernel."""
 import pytest
 import torch
 
@@ -74,4 +75,49 @@ def test_mismatched_device_tensors_are_refused():
             case()
             pytest.fail(f"case {i} was accepted")
     # and the well-formed call is still accepted
+    torch.cuda.synchronize()
+
+
+def test_overlap_detection_on_host_buffers():
+    """The overlap rule itself, on host memory (no device needed)."""
+    from block_sparse_attention_pack_amd._lib import _disjoint
+    buf = torch.zeros(1000, dtype=torch.uint8)
+    a, b, c = buf[:400], buf[400:800], buf[399:401]
+    _disjoint({"a": a}, {"b": b})                     # adjacent, disjoint
+    _disjoint({"a": a, "b": b}, {})
+    _disjoint({"e": buf[:0]}, {"a": a})               # empty tensors overlap nothing
+    with pytest.raises(ValueError, match="a overlaps c"):
+        _disjoint({"a": a}, {"c": c})
+    with pytest.raises(ValueError, match="b overlaps c"):
+        _disjoint({"b": b}, {"c": c})
+    with pytest.raises(ValueError, match="a overlaps b"):
+        _disjoint({"a": buf[:401], "b": b}, {})       # two outputs
+
+
+@pytest.mark.gpu
+def test_outputs_overlapping_inputs_are_refused():
+    dev = "cuda"
+    B, S, Hq, Hkv, D = 1, 100, 4, 2, 64
+    m = A.BlockMap(B, S, *A.fwd_tile(Hq, Hkv, D))
+    km = A.BlockMap(B, S, *A.bwd_tile(Hq, Hkv, D))
+    q, k, v = _bf(B, S, Hq, D, device=dev), _bf(B, S, Hkv, D, device=dev), _bf(B, S, Hkv, D, device=dev)
+    o, do = _bf(B, S, Hq, D, device=dev), _bf(B, S, Hq, D, device=dev)
+    lse = torch.zeros((B, Hq, S), device=dev)
+    need = A.workspace_bytes(B, S, Hq, D) + 256
+    big = torch.zeros(need + q.numel() * 2, dtype=torch.uint8, device=dev)
+    do_in_ws = big[need:].view(torch.bfloat16).view(q.shape)
+    dkv = k.clone()
+    cases = [
+        lambda: A.packed_attn_fwd(m, q, k, v, out=(q, lse)),                                   # o is q
+        lambda: A.packed_attn_fwd_rope(m, q, k, v, 1e4, q_rot_out=q),                          # q_rot is q
+        lambda: A.packed_attn_bwd(m, km, q, k, v, o, lse, do, out=(q, k.clone(), v.clone())),  # dq is q
+        lambda: A.packed_attn_bwd(m, km, q, k, v, o, lse, do, out=(do, k.clone(), v.clone())),  # dq is dout
+        lambda: A.packed_attn_bwd(m, km, q, k, v, o, lse, do, out=(q.clone(), dkv, dkv)),        # dk is dv
+        lambda: A.packed_attn_bwd(m, km, q, k, v, o, lse, do_in_ws, workspace=big),            # workspace holds dout
+        lambda: A.packed_attn_bwd_noalloc(m, km, q, k, v, o, lse, do, out=(o, k.clone(), v.clone())),
+    ]
+    for i, case in enumerate(cases):
+        with pytest.raises(ValueError, match="overlaps"):
+            case()
+            pytest.fail(f"case {i} was accepted")
     torch.cuda.synchronize()
