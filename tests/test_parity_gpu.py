@@ -147,11 +147,11 @@ def test_random_layout_sweep(seed):
     _check_full(w, run_fwd_bwd(w), f"sweep {seed}")
 
 
-@pytest.mark.parametrize("heads", [(64, 8, 128), (16, 16, 64), (40, 8, 64)])
+@pytest.mark.parametrize("heads", [(64, 8, 128), (16, 16, 64), (40, 8, 64), (32, 1, 64), (16, 2, 128)])
 def test_many_heads(heads):
-    """More q heads per workgroup grid (64 q heads over 8 kv heads), one kv
-    head per q head, and G = 5 (one q head per workgroup) on a two-row
-    layout whose lengths end inside tiles."""
+    """More q heads (64 over 8 kv heads), one kv head per q head, G = 5 (one
+    q head per workgroup), 32 q heads sharing one kv head and G = 8, on a
+    two-row layout whose lengths end inside tiles."""
     ps = PackSet(2, 333, [Pack(0, 0, 100, (90, 77)), Pack(0, 270, 20, (13, 30)), Pack(1, 5, 0, (64, 199))])
     w = make_workload(None, 9, packset=ps, heads=heads)
     say("parity many heads", heads)
