@@ -11,19 +11,19 @@
 //             workgroup = one query tile x WGH q heads of one kv group, one
 //             wave = 32 queries of one head.  Its prologue stages the Q and
 //             dO blocks (O straight into registers), forms
-//             Delta = rowsum(dO * O), then stages the first K/V tile; it
-//             writes -Delta and -LSE / scale (0 where the row sees nothing)
-//             for bwd_dkdv; then it walks the
-//             query tile's key tiles: S^T = K Q^T, dP^T = V dO^T, dS^T,
-//             dQ^T += K^T dS^T, the two 32-key halves of a tile staggered.
+//             Delta = rowsum(dO * O) and stages the first K/V tile; it writes
+//             -Delta and -LSE / scale (0 where the row sees nothing) for
+//             bwd_dkdv.  Then it walks the query tile's key tiles:
+//             S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T, the two
+//             32-key halves of a tile staggered.
 //   bwd_dkdv  key-major, on a map with 64-query x 128-key tiles.  A
 //             workgroup = one key tile x one kv group, 8 waves (32 keys x one
 //             32-query half each); K and V of the 128 keys stay in LDS, a
-//             wave's K operands, dK^T and dV^T in registers.  It walks the key
-//             tile's query
-//             tiles and, for each q head of the group, S = Q K^T, dP = dO V^T,
-//             dV^T += dO^T P, dK^T += Q^T dS, summing over the group's heads;
-//             the two query halves' partial sums meet in LDS at the end.
+//             wave's K operands, dK^T and dV^T in registers.  It walks the
+//             key tile's query tiles and, for each q head of the group,
+//             S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS, summing
+//             over the group's heads; the two query halves' partial sums meet
+//             in LDS at the end.
 //             Key tiles with a list longer than the average load of one
 //             workgroup slot (the prompt tiles of a pack shared by many
 //             responses) are split between two workgroups, whose fp32 sums
