@@ -37,7 +37,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kOrderThreads = 1024;
 constexpr int kOrderLds = 2048;  // tiles per side sorted in LDS; more use the chunked path
-constexpr int kTilesThreads = 1024;
+constexpr int kTilesThreads = 512;
 constexpr int kTilesWaves = kTilesThreads / 64;  // lists per map_tiles block
 
 struct MapOut {
