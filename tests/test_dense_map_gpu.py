@@ -42,3 +42,25 @@ def test_dense_map_baseline_matches_the_oracle(heads):
     assert max(errs.values()) <= 1e-2, errs
     assert float((lse[vl] - L[vl]).abs().max()) <= 1e-3
     assert torch.isneginf(lse[~vl]).all() and (r.o.cpu()[~valid] == 0).all()
+
+
+def test_backward_stages_one_at_a_time_equal_the_whole_backward():
+    """pba_packed_attn_bwd_stages with the dQ stage, then the dK/dV stage
+    (the way bench.py times them) gives bit-identical gradients to one call
+    with both stages."""
+    A = api()
+    w = make_workload(5, 0)  # the group packs: split key tiles included
+    q, k, v, do = (x.cuda().contiguous() for x in (w.q, w.k, w.v, w.do))
+    r = bench.Runner(A, torch, w.packset, q, k, v, do, w.Hq, w.Hkv, w.D, w.scale)
+    r.build_maps()
+    r.fwd()
+    r.bwd(A.BWD_ALL)
+    torch.cuda.synchronize()
+    whole = [t.clone() for t in (r.dq, r.dk, r.dv)]
+    for t in (r.dq, r.dk, r.dv):
+        t.fill_(float("nan"))
+    r.bwd(A.BWD_DQ)
+    r.bwd(A.BWD_DKDV)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), whole, (r.dq, r.dk, r.dv)):
+        assert torch.equal(a, b), name
