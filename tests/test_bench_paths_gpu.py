@@ -1,8 +1,10 @@
-"""The dense-map baseline (every tile pair visited as a partial tile, so the
-kernels evaluate the mask everywhere, including tiles where it removes every
-pair) against the oracle: the baseline bench.py compares the sparse path
-with must compute the same attention, and it drives the masked code paths
-through tiles that the sparse map would skip."""
+"""The ways bench.py runs the kernels besides the plain step.  The dense-map
+baseline (every tile pair visited as a partial tile, so the kernels evaluate
+the mask everywhere, including tiles where it removes every pair) against
+the oracle: the baseline the sparse path is compared with must compute the
+same attention, and it drives the masked code paths through tiles that the
+sparse map would skip.  The backward's two stages run one at a time, as
+bench.py times them."""
 import numpy as np
 import pytest
 import torch
